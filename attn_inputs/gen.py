@@ -1,0 +1,74 @@
+"""Seeded generation and storage-dtype rounding (no attention arithmetic here)."""
+from concurrent.futures import ThreadPoolExecutor
+import os
+
+import numpy as np
+
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2}
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+    out = r.astype(np.uint32).view(np.float32)
+    nan = np.isnan(x)
+    if nan.any():
+        out = out.copy()
+        out[nan] = np.nan
+    return out
+
+
+def fp16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest float16 (numpy's cast is RNE); returns float32."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_round(x)
+    if dtype == "f16":
+        return fp16_round(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+
+
+def slice_values(cid: int, tensor: str, b: int, h: int, n: int, d: int, sigma: float,
+                 dtype: str) -> np.ndarray:
+    """One [n, d] slice (batch b, head h) of tensor 'q' | 'k' | 'v' as exact float32 values."""
+    x = _rng(31, cid, TENSOR_IDS[tensor], b, h).standard_normal((n, d), dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return round_to_dtype(x, dtype)
+
+
+def tensor_values(cfg, tensor: str, threads: int | None = None) -> np.ndarray:
+    """A whole [B, H, N, d] tensor of a config as exact float32 values (threaded per slice)."""
+    H = cfg.H_q if tensor == "q" else cfg.H_kv
+    N = cfg.N_q if tensor == "q" else cfg.N_kv
+    out = np.empty((cfg.B, H, N, cfg.d), dtype=np.float32)
+
+    def fill(bh):
+        b, h = divmod(bh, H)
+        out[b, h] = slice_values(cfg.cid, tensor, b, h, N, cfg.d, cfg.sigma, cfg.dtype)
+
+    nthr = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(nthr) as ex:
+        list(ex.map(fill, range(cfg.B * H)))
+    return out
+
+
+def random_tensor(shape, seed: int, dtype: str, sigma: float = 1.0) -> np.ndarray:
+    """A small ad-hoc seeded tensor (for tests that are not one of the five configs)."""
+    x = _rng(31, 1000, seed).standard_normal(shape, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return round_to_dtype(x, dtype)

@@ -1,0 +1,7 @@
+"""Float64 CPU oracle for exact attention. TEST INFRASTRUCTURE ONLY: imported by
+the tests, the smoke check and the benchmark's CPU-baseline leg, never by the
+HIP library or its Python binding."""
+from .attention import (  # noqa: F401
+    MiB, attention_flops, kv_cache_bytes, attention_head_rows, attention_ref, score_bytes, softmax_weights,
+    visible_pairs,
+)

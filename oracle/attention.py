@@ -1,0 +1,173 @@
+"""Float64 CPU oracle for exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module; the HIP library never
+does, and it shares no code with it.
+
+What it computes (the plain definition, written out):
+
+* Attention is softmax(Q K^T / sqrt(d_k)) V: scores from Q and K, a row-wise
+  softmax, then a weighted average of V (auturnal.com transformer-attention
+  guide, section 2; marketmaker.cc "Flash Attention und die Frage nach der
+  Sequenzlaenge", section "Warum Aufmerksamkeit gedaechtnisgebunden ist").
+* It follows the standard (materialising) attention of the papanda925.com
+  survey, "標準Attention計算の擬似コード": form the score matrix, set masked
+  entries to -inf, apply softmax over the key axis, multiply by V. Heads are an
+  independent batch axis; tensors are [batch, heads, seq, head_dim].
+* The softmax subtracts the row maximum before exponentiating; the guide's
+  section 8 notes that this changes only the representation, not the
+  probabilities. Here it is the plain two-pass form (max, then exp and sum),
+  never the blockwise online recurrence.
+* Grouped-query attention: G = H_q / H_kv query heads share one KV head
+  (code-journey.com attention co-design summary, "Group Size(G)"); query head
+  h reads KV head h // G (contiguous groups).
+* Causal masking hides keys "in the future" of a query (marketmaker.cc,
+  section on causal masking). With N_q queries against n keys the last query
+  is aligned with the last key: key j is visible to query i iff
+  j <= i + (n - N_q). For N_q == n this is j <= i; for a single decode query it
+  is every cached key.
+* Decode reads a KV cache of capacity N_kv of which the first kv_lens[b]
+  positions are valid (guide section 9; papanda925.com "KVキャッシュ管理の概念").
+* A row with no visible key has output 0 and log-sum-exp -inf.
+* lse = m + ln(l), the per-row statistics that the backward pass keeps
+  (marketmaker.cc, "Rückwärtsdurchlauf").
+
+All arithmetic is float64 on the exact (dtype-rounded) input values; numpy's
+matmul (BLAS dgemm) forms the score rows and the weighted sum.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MiB = 2 ** 20
+
+
+def score_bytes(n: int, bytes_per: int = 4) -> int:
+    """Bytes to store one layer-head's n x n score matrix explicitly.
+
+    The guide's section 4 gives n^2 x 4 bytes for float32 scores, and its
+    section 6 tabulates 1, 4, 16, 64 MiB at n = 512, 1024, 2048, 4096.
+    """
+    return n * n * bytes_per
+
+
+def kv_cache_bytes(layers: int, n: int, h_kv: int, d_h: int, bytes_per: int) -> int:
+    """Approximate KV-cache size 2 * L * n * h_kv * d_h * b (keys and values of every
+    past position in every layer; weights, workspace and fragmentation excluded),
+    per the guide's section 9."""
+    return 2 * layers * n * h_kv * d_h * bytes_per
+
+
+def visible_pairs(N_q: int, n: int, causal: bool) -> int:
+    """Number of (query, key) pairs that enter the softmax for one head.
+
+    Counted by the definition above (bottom-right causal alignment). Each
+    visible pair costs one exponential (code-journey.com, softmax op count,
+    "Head Dimension(Hsz)"); causal skipping saves about half the work
+    (marketmaker.cc, causal masking section).
+    """
+    if not causal:
+        return N_q * n
+    off = n - N_q
+    total = 0
+    for i in range(N_q):
+        total += max(0, min(n, i + off + 1))
+    return total
+
+
+def _head(q_rows: np.ndarray, rows: np.ndarray, N_q: int, k: np.ndarray, v: np.ndarray,
+          causal: bool, scale: float, n: int, row_block: int = 512):
+    """One head. q_rows [len(rows), d] are the queries at sequence positions `rows`
+    (of N_q in all); k/v [>=n, d] with the first n rows valid. Returns (o, lse)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    d_v = v.shape[1]
+    o = np.zeros((len(rows), d_v), dtype=np.float64)
+    lse = np.full(len(rows), -np.inf, dtype=np.float64)
+    if n == 0 or len(rows) == 0:
+        return o, lse
+    kk = np.asarray(k[:n], dtype=np.float64)
+    vv = np.asarray(v[:n], dtype=np.float64)
+    off = n - N_q
+    keys = np.arange(n)
+    for s in range(0, len(rows), row_block):
+        r = rows[s:s + row_block]
+        qq = np.asarray(q_rows[s:s + row_block], dtype=np.float64)
+        # 1. materialise the score rows
+        scores = (qq @ kk.T) * float(scale)
+        # 2. mask: keys after the aligned diagonal are -inf
+        if causal:
+            masked = keys[None, :] > (r[:, None] + off)
+            scores = np.where(masked, -np.inf, scores)
+        # 3. two-pass softmax over the key axis
+        m = scores.max(axis=1)
+        empty = ~np.isfinite(m)            # no visible key
+        m_safe = np.where(empty, 0.0, m)
+        p = np.exp(scores - m_safe[:, None])
+        l = p.sum(axis=1)
+        # 4. weighted sum of V, normalised
+        with np.errstate(invalid="ignore", divide="ignore"):
+            out = (p @ vv) / l[:, None]
+            row_lse = m_safe + np.log(l)
+        out[empty] = 0.0
+        row_lse[empty] = -np.inf
+        o[s:s + row_block] = out
+        lse[s:s + row_block] = row_lse
+    return o, lse
+
+
+def attention_ref(q, k, v, causal: bool, scale: float, kv_lens=None, row_block: int = 512):
+    """Exact attention in float64.
+
+    q: [B, H_q, N_q, d]; k, v: [B, H_kv, N_kv, d] (any float dtype; exact values).
+    kv_lens: optional per-batch valid key counts (each in [0, N_kv]); default N_kv.
+    Returns (o [B, H_q, N_q, d] float64, lse [B, H_q, N_q] float64, natural log).
+    """
+    B, H_q, N_q, d = q.shape
+    Bk, H_kv, N_kv, dk = k.shape
+    if Bk != B or dk != d or v.shape[:3] != k.shape[:3]:
+        raise ValueError("shape mismatch")
+    if H_q % H_kv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    G = H_q // H_kv
+    o = np.zeros((B, H_q, N_q, v.shape[3]), dtype=np.float64)
+    lse = np.zeros((B, H_q, N_q), dtype=np.float64)
+    rows = np.arange(N_q)
+    for b in range(B):
+        n = N_kv if kv_lens is None else int(kv_lens[b])
+        if not 0 <= n <= N_kv:
+            raise ValueError("kv_lens out of range")
+        for h in range(H_q):
+            g = h // G
+            o[b, h], lse[b, h] = _head(q[b, h], rows, N_q, k[b, g], v[b, g], causal, scale, n,
+                                       row_block)
+    return o, lse
+
+
+def attention_head_rows(q_rows, rows, N_q: int, k_head, v_head, causal: bool, scale: float,
+                        n: int | None = None):
+    """Selected output rows of one head, for sampled checks of full-size runs.
+
+    q_rows [len(rows), d] are the queries at positions `rows` of a sequence of N_q
+    queries; k_head/v_head [N_kv, d] hold the head's keys/values, of which the
+    first n (default all) are valid.
+    """
+    n = k_head.shape[0] if n is None else n
+    return _head(q_rows, rows, N_q, k_head, v_head, causal, scale, n, 256)
+
+
+def softmax_weights(scores: np.ndarray) -> np.ndarray:
+    """Row softmax of a score matrix (-inf entries get weight 0), float64, two-pass."""
+    s = np.asarray(scores, dtype=np.float64)
+    m = s.max(axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(s - m)
+    return p / p.sum(axis=-1, keepdims=True)
+
+
+def attention_flops(N_q: int, n: int, d: int, causal: bool) -> int:
+    """Algorithmic FLOPs for one query head: 2d for Q.K and 2d for P.V per visible pair."""
+    return 4 * d * visible_pairs(N_q, n, causal)
+
+
+__all__ = ["score_bytes", "kv_cache_bytes", "visible_pairs", "attention_ref", "attention_head_rows",
+           "softmax_weights", "attention_flops", "MiB"]
