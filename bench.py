@@ -1,0 +1,272 @@
+"""Benchmark: prefill attention TFLOP/s and decode KV GB/s on one MI355X.
+
+Default run (one JSON line on stdout):
+  * the step timed for `value` is one causal MHA prefill, bf16, B=4, H=32,
+    N=4096, d=128 (inputs resident in HBM), in TFLOP/s of algorithmic work
+    (4*d FLOP per visible query-key pair per query head);
+  * the decode half of the metric is timed the same way on GQA decode, bf16,
+    B=64, H_q=32, H_kv=4, d=128, 32768 cached tokens per request, in GB/s of
+    K and V bytes read, and reported under "decode";
+  * "roofline" relates the prefill kernel's rate (from HIP events on its launch
+    stream) to the bf16 MFMA peak; "decode_roofline" relates decode to HBM peak;
+  * "cpu_baseline" times the float64 oracle on a bounded sample of the prefill
+    workload on this host's cores.
+`--all` also times the other three workloads (fp32 single head, the 23,400-step
+fp16 series, causal GQA prefill at 32768) and ragged decode.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_16BIT = 2500.0   # TFLOP/s, dense bf16/fp16 MFMA, MI355X
+PEAK_MFMA_F32 = 157.3      # TFLOP/s, fp32 matrix
+PEAK_HBM = 8000.0          # GB/s, HBM3E
+
+# Context figures the pages print (quoted, with our recomputed values beside them).
+PAGE_CONTEXT = {
+    "prefill_ai_G8_ISL32768_as_printed": "~15,990 FLOP/B (formula 2*G*ISL/(G+1) gives 58,254.2)",
+    "decode_ai_G8_KVSL32768_as_printed": "~15.99 per FP8 KV element (formula gives 15.996)",
+    "decode_speedup_G1_to_G8_as_printed": "about 2x (FP8 KV cache, hardware not named)",
+    "fp16_score_matrix_23400_steps_12_heads_as_printed": "about 12.9 GB (23400^2*12*2 B = 13.14 GB)",
+}
+
+
+def visible_pairs(N_q: int, n: int, causal: bool) -> int:
+    """Visible (query, key) pairs for one head, bottom-right causal alignment (closed form)."""
+    if not causal:
+        return N_q * n
+    off = n - N_q
+    # rows i with i + off + 1 in [1, n]: count min(n, i + off + 1) for i + off + 1 > 0
+    total = 0
+    i0 = max(0, -off)  # first row that sees any key
+    i1 = min(N_q, n - off)  # rows below i1 see a prefix shorter than n
+    if i1 > i0:
+        a, b = i0 + off + 1, i1 - 1 + off + 1
+        total += (a + b) * (i1 - i0) // 2
+    if N_q > max(i1, i0):
+        total += n * (N_q - max(i1, i0))
+    return total
+
+
+def prefill_flops(cfg) -> int:
+    return 4 * cfg.d * cfg.B * cfg.H_q * visible_pairs(cfg.N_q, cfg.N_kv, cfg.causal)
+
+
+def decode_kv_bytes(cfg, lens) -> int:
+    es = 2 if cfg.dtype in ("bf16", "f16") else 4
+    return int(np.sum(lens, dtype=np.int64)) * cfg.H_kv * cfg.d * 2 * es
+
+
+def make_device_tensor(cfg, name, torch, threads=16):
+    import attn_inputs as A
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+    H = cfg.H_q if name == "q" else cfg.H_kv
+    N = cfg.N_q if name == "q" else cfg.N_kv
+    t = torch.empty((cfg.B, H, N, cfg.d), dtype=dt, device="cuda")
+
+    def gen(bh):
+        b, h = divmod(bh, H)
+        return b, h, A.slice_values(cfg.cid, name, b, h, N, cfg.d, cfg.sigma, cfg.dtype)
+
+    with ThreadPoolExecutor(threads) as ex:
+        for b, h, x in ex.map(gen, range(cfg.B * H)):
+            t[b, h] = torch.from_numpy(x).to("cuda").to(dt)
+    return t
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Warm up, then time exactly `steps` calls with HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def bench_prefill(cfg, steps, warmup, torch, E):
+    q = make_device_tensor(cfg, "q", torch)
+    k = make_device_tensor(cfg, "k", torch)
+    v = make_device_tensor(cfg, "v", torch)
+    o = torch.empty_like(q)
+    t_first = time.perf_counter()
+    E.attn_prefill_fwd(q, k, v, o, causal=cfg.causal, scale=cfg.scale)
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t_first) * 1e3
+    ms, wall = time_launches(lambda: E.attn_prefill_fwd(q, k, v, o, causal=cfg.causal, scale=cfg.scale),
+                             steps, warmup, torch)
+    flops = prefill_flops(cfg)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_F32 if cfg.dtype == "f32" else PEAK_MFMA_16BIT
+    del q, k, v, o
+    return {"config": cfg.cid, "name": cfg.name, "ms": ms, "tflops": tflops, "flops": flops,
+            "frac_of_peak": tflops / peak, "peak_tflops": peak, "first_call_ms": first_ms,
+            "wall_s": wall}
+
+
+def bench_decode(cfg, steps, warmup, torch, E, ragged=False):
+    import attn_inputs as A
+    lens = A.ragged_lengths(cfg) if ragged else np.full(cfg.B, cfg.N_kv, np.int32)
+    q = make_device_tensor(cfg, "q", torch)
+    k = make_device_tensor(cfg, "k", torch)
+    v = make_device_tensor(cfg, "v", torch)
+    o = torch.empty_like(q)
+    lens_d = torch.from_numpy(lens).cuda()
+    ws = torch.empty(E.attn_decode_workspace_size(cfg.B, cfg.H_q, cfg.H_kv, 1, cfg.N_kv, cfg.d, q.dtype),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        E.attn_decode_fwd(q, k, v, o, kv_lens=lens_d, scale=cfg.scale, workspace=ws)
+
+    ms, wall = time_launches(call, steps, warmup, torch)
+    nbytes = decode_kv_bytes(cfg, lens)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del q, k, v, o, ws
+    return {"config": "5r" if ragged else 5, "name": cfg.name, "ms": ms, "kv_bytes": nbytes,
+            "gb_per_s": gbs, "frac_of_peak": gbs / PEAK_HBM, "peak_gb_per_s": PEAK_HBM,
+            "wall_s": wall}
+
+
+def cpu_baseline(cfg, budget_s=15.0):
+    """The float64 oracle on a bounded sample of the prefill workload (whole heads)."""
+    import attn_inputs as A
+    from oracle import attention_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        threads = 1
+    heads_done, elapsed = 0, 0.0
+    t_start = time.perf_counter()
+    while elapsed < budget_s and heads_done < cfg.B * cfg.H_q:
+        b, h = divmod(heads_done, cfg.H_q)
+        q = A.slice_values(cfg.cid, "q", b, h, cfg.N_q, cfg.d, cfg.sigma, cfg.dtype)
+        g = h // cfg.G
+        k = A.slice_values(cfg.cid, "k", b, g, cfg.N_kv, cfg.d, cfg.sigma, cfg.dtype)
+        v = A.slice_values(cfg.cid, "v", b, g, cfg.N_kv, cfg.d, cfg.sigma, cfg.dtype)
+        t0 = time.perf_counter()
+        attention_ref(q[None, None], k[None, None], v[None, None], cfg.causal, cfg.scale)
+        elapsed += time.perf_counter() - t0
+        heads_done += 1
+        if time.perf_counter() - t_start > 4 * budget_s:
+            break
+    flops = 4 * cfg.d * heads_done * visible_pairs(cfg.N_q, cfg.N_kv, cfg.causal)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads_done} of {cfg.B * cfg.H_q} heads (full {cfg.N_q}-row causal heads, "
+                      f"float64 numpy, {elapsed:.1f} s)",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--all", action="store_true", help="also time configs 1, 3, 4 and ragged decode")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
+              f"multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import torch
+    import attn_inputs as A
+    import exact_attention_31_amd as E
+    E.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 3
+    props = torch.cuda.get_device_properties(0)
+
+    res = {}
+    if args.only in (None, "prefill"):
+        res["prefill"] = bench_prefill(A.CONFIGS[2], args.steps, args.warmup, torch, E)
+        print(f"# prefill c2: {res['prefill']['ms']:.3f} ms  {res['prefill']['tflops']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+    if args.only in (None, "decode"):
+        res["decode"] = bench_decode(A.CONFIGS[5], args.steps, args.warmup, torch, E)
+        print(f"# decode c5: {res['decode']['ms']:.3f} ms  {res['decode']['gb_per_s']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+    extra = []
+    if args.all:
+        for cid in (1, 3, 4):
+            r = bench_prefill(A.CONFIGS[cid], max(5, args.steps // 5) if cid == 4 else args.steps,
+                              args.warmup, torch, E)
+            extra.append(r)
+            print(f"# prefill c{cid}: {r['ms']:.3f} ms  {r['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        r = bench_decode(A.CONFIGS[6], args.steps, args.warmup, torch, E, ragged=True)
+        extra.append(r)
+        print(f"# decode c5 ragged: {r['ms']:.3f} ms  {r['gb_per_s']:.0f} GB/s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu and "prefill" in res:
+        cpu = cpu_baseline(A.CONFIGS[2], args.cpu_budget)
+
+    p = res.get("prefill")
+    d = res.get("decode")
+    main_r = p if p is not None else d
+    line = {
+        "metric": "prefill attention TFLOP/s and decode KV GB/s, as % of MI355X MFMA/HBM peak",
+        "value": round(p["tflops"], 3) if p else round(d["gb_per_s"], 3),
+        "unit": "TFLOP/s" if p else "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(main_r["ms"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "causal MHA prefill, bf16, B=4, H_q=H_kv=32, N=4096, d=128"
+                   if p else "GQA decode, bf16, B=64, H_q=32, H_kv=4, d=128, KV 32768",
+                   "B": 4 if p else 64, "seq_len": 4096 if p else 32768, "head_dim": 128,
+                   "causal": bool(p), "parallelism": "single GPU"},
+    }
+    if p:
+        line["roofline"] = {"bound": "mfma", "achieved": round(p["tflops"], 3), "peak": PEAK_MFMA_16BIT,
+                            "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_MFMA_16BIT, 4),
+                            "traffic": None, "kernel": "prefill16_kernel<BF16,128,causal>",
+                            "work_per_launch": p["flops"]}
+    if d:
+        line["decode"] = {"workload": "GQA decode, bf16, B=64, H_q=32, H_kv=4 (G=8), d=128, "
+                                      "KV 32768 per request", "ms_per_step": round(d["ms"], 5),
+                          "value": round(d["gb_per_s"], 2), "unit": "GB/s",
+                          "frac_of_hbm_peak": round(d["frac_of_peak"], 4)}
+        line["decode_roofline"] = {"bound": "hbm", "achieved": round(d["gb_per_s"], 2), "peak": PEAK_HBM,
+                                   "unit": "GB/s", "frac": round(d["frac_of_peak"], 4), "traffic": None,
+                                   "kernel": "decode_split_kernel + decode_merge_kernel (one step)",
+                                   "work_per_launch": d["kv_bytes"]}
+    if p:
+        line["prefill_first_call_ms"] = round(p["first_call_ms"], 3)
+    if cpu:
+        line["cpu_baseline"] = cpu
+    if extra:
+        line["other_workloads"] = [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}
+                                   for r in extra]
+    line["device"] = {"name": props.name, "cus": props.multi_processor_count,
+                      "arch": getattr(props, "gcnArchName", "")}
+    line["page_context"] = PAGE_CONTEXT
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,177 @@
+"""Exact scaled-dot-product attention for MI355X (gfx950): Python binding.
+
+Argument marshalling only: every computation runs in the HIP kernels of the
+C-ABI library libattn.so (declared in include/attn.h). PyTorch provides device
+memory and the current stream. If the library is missing, importing works but
+every call raises; there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+DTYPE_CODE = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_GQA",
+    4: "ATTN_ERR_UNSUPPORTED", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_LAUNCH",
+    7: "ATTN_ERR_NO_DEVICE", 8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_VALUE",
+}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({attn_status_string(status)})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libattn.so (raises ImportError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m exact_attention_31_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_prefill_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.attn_prefill_fwd.restype = i
+    lib.attn_decode_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.attn_decode_workspace_size.restype = sz
+    lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_decode_fwd.restype = i
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = i
+    _lib = lib
+    return lib
+
+
+def attn_status_string(status: int) -> str:
+    return load().attn_status_string(int(status)).decode()
+
+
+def attn_version() -> int:
+    return load().attn_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check_tensor(name, t, dtype, device, ndim=4):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda" or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-D tensor")
+
+
+def attn_prefill_fwd(q, k, v, o=None, lse=None, *, causal: bool = False, scale: float | None = None,
+                     return_lse: bool = False, stream=None):
+    """O = softmax(scale * Q K^T) V on the GPU (q [B,H_q,N_q,d], k/v [B,H_kv,N_kv,d]).
+
+    Allocates o (and lse when return_lse) with torch if not given. Returns o, or (o, lse).
+    """
+    lib = load()
+    if q.dtype not in DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _check_tensor("q", q, q.dtype, dev)
+    _check_tensor("k", k, q.dtype, dev)
+    _check_tensor("v", v, q.dtype, dev)
+    B, H_q, N_q, d = q.shape
+    _, H_kv, N_kv, _ = k.shape
+    if tuple(k.shape) != (B, H_kv, N_kv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor("o", o, q.dtype, dev)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, dev, ndim=3)
+        if tuple(lse.shape) != (B, H_q, N_q):
+            raise ValueError("lse must be [B, H_q, N_q]")
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(dev):
+        st = lib.attn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H_q, H_kv, N_q,
+                                  N_kv, d, int(bool(causal)), float(scale), DTYPE_CODE[q.dtype],
+                                  _stream(dev, stream))
+    if st != 0:
+        raise AttnError(st, "attn_prefill_fwd")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_decode_workspace_size(B, H_q, H_kv, N_q, N_kv, d, dtype) -> int:
+    code = DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load().attn_decode_workspace_size(B, H_q, H_kv, N_q, N_kv, d, code))
+
+
+def attn_decode_fwd(q, k_cache, v_cache, o=None, *, kv_lens=None, lse=None, causal: bool = False,
+                    scale: float | None = None, workspace=None, return_lse: bool = False,
+                    stream=None):
+    """Split-KV GQA decode: q [B,H_q,1,d] against caches [B,H_kv,N_kv,d] with kv_lens [B] int32."""
+    lib = load()
+    if q.dtype not in DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _check_tensor("q", q, q.dtype, dev)
+    _check_tensor("k_cache", k_cache, q.dtype, dev)
+    _check_tensor("v_cache", v_cache, q.dtype, dev)
+    B, H_q, N_q, d = q.shape
+    _, H_kv, N_kv, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, H_kv, N_kv, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if kv_lens is not None:
+        _check_tensor("kv_lens", kv_lens, torch.int32, dev, ndim=1)
+        if kv_lens.shape[0] != B:
+            raise ValueError("kv_lens must have B entries")
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor("o", o, q.dtype, dev)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, dev, ndim=3)
+    need = attn_decode_workspace_size(B, H_q, H_kv, N_q, N_kv, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(dev):
+        st = lib.attn_decode_fwd(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens), _ptr(o),
+                                 _ptr(lse), B, H_q, H_kv, N_q, N_kv, d, int(bool(causal)),
+                                 float(scale), DTYPE_CODE[q.dtype], _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_fwd")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+__all__ = ["attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_size", "attn_status_string",
+           "attn_version", "load", "AttnError", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

@@ -1,0 +1,83 @@
+// Device-side building blocks for the gfx950 (CDNA4) attention kernels.
+//
+// Matrix-core conventions used throughout (64-lane wavefront):
+//   v_mfma_f32_32x32x16_{bf16,f16}: lane l supplies row (l % 32) of A and column
+//   (l % 32) of B, each as 8 consecutive K-slots of half (l / 32); the 16
+//   accumulators of lane l hold column (l % 32) of D at rows
+//   8*(r/4) + 4*(l/32) + (r%4), r = 0..15.
+//   v_mfma_f32_16x16x32_{bf16,f16}: lane l supplies row/column (l % 16) with
+//   the 8 K-slots of quarter (l / 16); accumulator r of lane l is D[4*(l/16)+r][l%16].
+//   v_mfma_f32_32x32x2_f32: lane l supplies A[l%32][l/32] and B[l/32][l%32].
+// A and B always agree on which K index a (lane half, slot) pair carries, so a
+// contraction may permute its K index freely as long as both operands use the
+// same permutation; the kernels rely on this to feed softmax probabilities from
+// the accumulator layout straight back into the next MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// 16-bit element traits: bf16 or fp16 storage, fp32 accumulation.
+struct BF16 {
+  static __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  // Round two floats to nearest-even 16-bit values and pack (lo in bits 0..15).
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+struct F16 {
+  static __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f16x2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Exchange with the lane 32 positions away (the other half of the wavefront).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// LDS transposing read (gfx950 ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane i addresses 4 consecutive 16-bit elements of row i/4, columns
+// 4*(i%4)..+3, of a 4 x 16 block; lane i receives column i of that block, i.e.
+// the 4 elements of rows 0..3 at column i, packed low to high.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+}  // namespace attn

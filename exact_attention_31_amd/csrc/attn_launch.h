@@ -1,0 +1,53 @@
+// Host-side launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeF16 = 1;
+constexpr int kDtypeBF16 = 2;
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H_q, H_kv, N_q, N_kv, d;
+  int causal;
+  float scale;
+  int dtype;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int* kv_lens;  // device pointer or null (all N_kv)
+  void* o;
+  float* lse;
+  int B, H_q, H_kv, N_kv, d;
+  float scale;
+  int dtype;
+  int chunk;   // keys per split
+  int splits;  // splits per (request, KV head), = ceil(N_kv / chunk)
+  float* part_u;   // [B, H_q, splits, d] un-normalised partial outputs
+  float* part_ml;  // [B, H_q, splits, 2] partial (max in log2 units, denominator)
+};
+
+// Split plan shared by the workspace query and the launch.
+struct DecodePlan {
+  int chunk;
+  int splits;
+  size_t workspace_bytes;
+};
+DecodePlan decode_plan(int B, int H_q, int H_kv, int N_kv, int d);
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace attn

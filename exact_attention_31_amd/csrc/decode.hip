@@ -1,0 +1,259 @@
+// Decode attention forward on gfx950: one query token per request against a
+// KV cache, grouped-query (G = H_q / H_kv query heads share a KV head).
+//
+// Decode is the phase whose matrix product has only G rows and which is bound by
+// HBM bandwidth (code-journey.com attention co-design summary, prefill/decode
+// table and "Group Size(G)"): every cached key and value byte is read once and
+// reused by the G query heads of its group. To give 256 compute units enough
+// independent streams, the KV sequence is split into chunks; each chunk yields
+// per-head partial statistics (max m_s, denominator l_s, un-normalised output
+// u_s), and a second kernel merges them with weights exp(m_s - m), the same
+// rescaling that the online softmax applies between blocks (auturnal.com
+// transformer-attention guide, section 8), applied across partitions.
+//
+// gfx950 mapping: a workgroup (4 wavefronts) takes one (request, KV head,
+// chunk); each wavefront takes 32 keys per step. K rows go straight from HBM
+// into the A operand of S^T = K Q^T (v_mfma_f32_16x16x32, 16-byte loads); the
+// group's query heads form the B operand (padded to 16 columns). V rows are
+// staged in LDS and read back transposed (ds_read_b64_tr_b16) as the A operand
+// of O^T = V^T P^T, so each lane's accumulators belong to one query head.
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaveKeys = 32;            // keys per wavefront step
+constexpr int kStepKeys = 4 * kWaveKeys; // keys per workgroup step
+constexpr int kQCols = 16;               // query heads per workgroup (MFMA N)
+
+template <class TT, int D>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const int* __restrict__ kv_lens, float* __restrict__ part_u, float* __restrict__ part_ml,
+    int H_q, int H_kv, int N_kv, int splits, int chunk, float scale_log2) {
+  constexpr int VST = D + 16;       // LDS row stride of the staged V rows
+  constexpr int KS = D / 32;        // k-steps of the score MFMA
+  constexpr int DB = D / 16;        // 16-wide output blocks
+  constexpr int kV = 4 * kWaveKeys * VST;          // V staging (elements)
+  constexpr int kComb = 4 * kQCols * (D + 2) * 2;  // combine area, in 16-bit units
+  constexpr int kLds = kV > kComb ? kV : kComb;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kLds];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15;   // query column (S^T) / output head
+  const int g = lane >> 4;     // 16-lane group
+  const int split = blockIdx.x;
+  const int G = H_q / H_kv;
+  const int ngroups = (G + kQCols - 1) / kQCols;
+  const int hk = blockIdx.y / ngroups;
+  const int qg = blockIdx.y % ngroups;
+  const int b = blockIdx.z;
+
+  int len = kv_lens ? kv_lens[b] : N_kv;
+  len = min(max(len, 0), N_kv);
+  const int start = split * chunk;
+  if (start >= len) return;  // nothing in this split (its partial is never read)
+  const int end = min(start + chunk, len);
+
+  const uint16_t* Kh = K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
+  const uint16_t* Vh = V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
+  const int hq0 = hk * G + qg * kQCols;       // first query head of this group
+  const int ncols = min(kQCols, G - qg * kQCols);
+
+  // Q^T operand: column c16 = query head hq0 + c16, K-slots d = 32*st + 8*g + 0..7
+  u32x4_t qreg[KS];
+  {
+    const bool ok = c16 < ncols;
+    const uint16_t* Qh = Q + ((int64_t)b * H_q + hq0 + c16) * D;
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      qreg[st] = ok ? *(const u32x4_t*)(Qh + 32 * st + 8 * g) : u32x4_t{0, 0, 0, 0};
+  }
+
+  f32x4_t oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x4_t{0, 0, 0, 0};
+  float m = kNegInf, l = 0.f;
+  uint16_t* sV = smem + wave * kWaveKeys * VST;
+
+  for (int t0 = start; t0 < end; t0 += kStepKeys) {
+    const int w0 = t0 + wave * kWaveKeys;  // this wavefront's first key
+    // ---- stage this wavefront's 32 V rows in LDS (zero past the end)
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int c = lane; c < kWaveKeys * CPR; c += 64) {
+      const int r = c / CPR, cc = c % CPR;
+      u32x4_t vv = {0, 0, 0, 0};
+      if (w0 + r < end) vv = *(const u32x4_t*)(Vh + (int64_t)(w0 + r) * D + cc * 8);
+      *(u32x4_t*)(sV + r * VST + cc * 8) = vv;
+    }
+    // ---- S^T = K Q^T for two 16-key blocks, K straight from HBM
+    f32x4_t s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = w0 + kb * 16 + c16;
+      u32x4_t a[KS];
+#pragma unroll
+      for (int st = 0; st < KS; ++st)
+        a[st] = (key < end) ? *(const u32x4_t*)(Kh + (int64_t)key * D + 32 * st + 8 * g)
+                            : u32x4_t{0, 0, 0, 0};
+      s[kb] = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) s[kb] = TT::mfma16(a[st], qreg[st], s[kb]);
+    }
+    // ---- mask keys past the end, running max over the wavefront's 32 keys
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = w0 + kb * 16 + 4 * g + r;
+        const float x = (key < end) ? s[kb][r] * scale_log2 : kNegInf;
+        s[kb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float m_ref = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_ref);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+    float p[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[kb][r] = fast_exp2(s[kb][r] - m_ref);
+        l += p[kb][r];
+      }
+    // K-slots of lane group g: keys 4g+0..3 (block 0) then 16+4g+0..3 (block 1)
+    const u32x4_t bop = {TT::pack2(p[0][0], p[0][1]), TT::pack2(p[0][2], p[0][3]),
+                         TT::pack2(p[1][0], p[1][1]), TT::pack2(p[1][2], p[1][3])};
+    __syncthreads();  // V rows of this step are in LDS
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int dcol = 16 * db + 4 * (c16 & 3);
+      const u32x2_t lo = lds_read_tr16(sV + (4 * g + (c16 >> 2)) * VST + dcol);
+      const u32x2_t hi = lds_read_tr16(sV + (16 + 4 * g + (c16 >> 2)) * VST + dcol);
+      const u32x4_t aop = {lo[0], lo[1], hi[0], hi[1]};
+      oacc[db] = TT::mfma16(aop, bop, oacc[db]);
+    }
+    __syncthreads();  // before the next step overwrites the V rows
+  }
+
+  // ---- combine the four wavefronts' partials through LDS
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  float* cm = (float*)smem;                 // [4][16] max
+  float* cl = cm + 4 * kQCols;              // [4][16] denominator
+  float* cu = cl + 4 * kQCols;              // [4][16][D] output
+  if (g == 0) {
+    cm[wave * kQCols + c16] = m;
+    cl[wave * kQCols + c16] = l;
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cu[(wave * kQCols + c16) * D + 16 * db + 4 * g + r] = oacc[db][r];
+  __syncthreads();
+  const int64_t row0 = ((int64_t)b * H_q + hq0) * splits + split;  // (b, hq0, split)
+  for (int e = tid; e < ncols * D; e += kThreads) {
+    const int c = e / D, d = e % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w * kQCols + c]);
+    const float Mref = (M == kNegInf) ? 0.f : M;
+    float L = 0.f, U = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = fast_exp2(cm[w * kQCols + c] - Mref);
+      L += wt * cl[w * kQCols + c];
+      U += wt * cu[(w * kQCols + c) * D + d];
+    }
+    const int64_t row = row0 + (int64_t)c * splits;
+    part_u[row * D + d] = U;
+    if (d == 0) {
+      part_ml[row * 2 + 0] = M;
+      part_ml[row * 2 + 1] = L;
+    }
+  }
+}
+
+template <class TT, int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(
+    const float* __restrict__ part_u, const float* __restrict__ part_ml,
+    const int* __restrict__ kv_lens, uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q,
+    int N_kv, int splits, int chunk) {
+  const int d = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y;
+  int len = kv_lens ? kv_lens[b] : N_kv;
+  len = min(max(len, 0), N_kv);
+  const int ns = (len + chunk - 1) / chunk;
+  const int64_t row0 = ((int64_t)b * H_q + h) * splits;
+  float M = kNegInf;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[(row0 + s) * 2]);
+  const float Mref = (M == kNegInf) ? 0.f : M;
+  float L = 0.f, U = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float wt = fast_exp2(part_ml[(row0 + s) * 2] - Mref);
+    L += wt * part_ml[(row0 + s) * 2 + 1];
+    U += wt * part_u[(row0 + s) * D + d];
+  }
+  const float o = (L > 0.f) ? U / L : 0.f;
+  // 16-bit store: pair adjacent lanes
+  const float o_hi = __shfl_down(o, 1);
+  if ((d & 1) == 0) {
+    *(uint32_t*)(O + ((int64_t)b * H_q + h) * D + d) = TT::pack2(o, o_hi);
+  }
+  if (LSE != nullptr && d == 0) {
+    LSE[(int64_t)b * H_q + h] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
+  }
+}
+
+template <class TT, int D>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
+  const int G = a.H_q / a.H_kv;
+  const int ngroups = (G + kQCols - 1) / kQCols;
+  dim3 grid(a.splits, a.H_kv * ngroups, a.B);
+  hipLaunchKernelGGL((decode_split_kernel<TT, D>), grid, dim3(kThreads), 0, st,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.kv_lens,
+                     a.part_u, a.part_ml, a.H_q, a.H_kv, a.N_kv, a.splits, a.chunk,
+                     a.scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<TT, D>), dim3(a.H_q, a.B), dim3(D), 0, st, a.part_u,
+                     a.part_ml, a.kv_lens, (uint16_t*)a.o, a.lse, a.H_q, a.N_kv, a.splits, a.chunk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+DecodePlan decode_plan(int B, int H_q, int H_kv, int N_kv, int d) {
+  const int G = H_q / H_kv;
+  const int64_t units = (int64_t)B * H_kv * ((G + kQCols - 1) / kQCols);
+  // aim for about 8192 workgroups in all, chunks of at least 256 keys
+  int64_t want = (8192 + units - 1) / units;
+  if (want < 1) want = 1;
+  int64_t chunk = ((int64_t)N_kv + want - 1) / want;
+  chunk = ((chunk + kStepKeys - 1) / kStepKeys) * kStepKeys;
+  if (chunk < 256) chunk = 256;
+  DecodePlan p;
+  p.chunk = (int)chunk;
+  p.splits = N_kv > 0 ? (int)((N_kv + chunk - 1) / chunk) : 1;
+  p.workspace_bytes = (size_t)B * H_q * p.splits * (size_t)(d + 2) * sizeof(float);
+  return p;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  if (a.dtype == kDtypeBF16) return a.d == 64 ? launch_t<BF16, 64>(a, st) : launch_t<BF16, 128>(a, st);
+  return a.d == 64 ? launch_t<F16, 64>(a, st) : launch_t<F16, 128>(a, st);
+}
+
+}  // namespace attn

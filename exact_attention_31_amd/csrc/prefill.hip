@@ -1,0 +1,374 @@
+// Prefill attention forward on gfx950: O = softmax(scale * Q K^T) V, block by
+// block, without writing the score matrix to HBM.
+//
+// The method (marketmaker.cc "Flash Attention und die Frage nach der
+// Sequenzlaenge", sections on the algorithm, the online-softmax recurrence and
+// FA2; auturnal.com transformer-attention guide, section 8): each query block
+// keeps, per row, a running maximum m, a denominator l and an un-normalised
+// output u; a new key block raises the maximum to m', rescales l and u by
+// exp(m - m'), adds its own exponentials, and the row's output is u / l, divided
+// once at the end (FA2's first change). Query blocks are spread over the grid
+// (FA2's second change) and each wavefront owns whole query rows, so row
+// statistics never cross wavefronts (FA2's third change). Key blocks that lie
+// entirely after a causal query block are never loaded (causal skipping).
+//
+// gfx950 mapping (one workgroup = 4 wavefronts = 128 query rows):
+//   * Q rows stay in VGPRs for the whole loop, laid out as the B operand of
+//     S^T = K Q^T (v_mfma_f32_32x32x16): each lane owns one query row, and the
+//     accumulator layout then gives each lane 16 of the 32 scores of its row,
+//     so the row max/sum needs one exchange with the opposite half-wave only.
+//   * K and V tiles (64 keys) are staged through LDS with 16-byte coalesced
+//     loads; all four wavefronts read them.
+//   * The probabilities, rounded to the input type, are reused in registers as
+//     the B operand of O^T = V^T P^T; V^T comes from LDS through the gfx950
+//     transposing read, so each lane's output accumulators belong to its own
+//     query row and the rescale by exp2(m - m') is lane-local.
+//   * exp is evaluated as exp2 with scale*log2(e) folded into one multiply.
+// fp32 inputs use v_mfma_f32_32x32x2_f32 in the same arrangement (no LDS
+// transpose is needed there because each lane feeds one K-slot).
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int kBM = 128;  // query rows per workgroup (4 wavefronts x 32)
+constexpr int kBN = 64;   // keys per tile
+constexpr int kThreads = 256;
+
+// Row stride (elements) of the K and V tiles in LDS. The padding keeps the
+// 16-byte row reads of K and the 4-row transposing reads of V spread over banks.
+template <int D> struct Lds16 {
+  static constexpr int kK = D + 8;
+  static constexpr int kV = D + 16;
+};
+
+template <class TT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
+    float scale_log2, int nqb) {
+  constexpr int KST = Lds16<D>::kK;
+  constexpr int VST = Lds16<D>::kV;
+  constexpr int KS = D / 16;   // k-steps of the score MFMA
+  constexpr int DB = D / 32;   // 32-wide blocks of the output
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kBN * KST];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kBN * VST];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  // causal: longest query blocks first
+  const int qb = CAUSAL ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int hk = h / (H_q / H_kv);
+
+  const uint16_t* Qh = Q + ((int64_t)b * H_q + h) * (int64_t)N_q * D;
+  const uint16_t* Kh = K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
+  const uint16_t* Vh = V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
+
+  const int q0 = qb * kBM + wave * 32;  // first row of this wavefront
+  const int qrow = q0 + lr;             // this lane's row
+  const int off = N_kv - N_q;           // bottom-right causal alignment
+
+  u32x4_t qreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qreg[s] = (qrow < N_q) ? *(const u32x4_t*)(Qh + (int64_t)qrow * D + 16 * s + 8 * lh)
+                           : u32x4_t{0, 0, 0, 0};
+  }
+
+  int kv_end = N_kv;
+  if (CAUSAL) {
+    const int qlast = min(qb * kBM + kBM - 1, N_q - 1);
+    kv_end = min(N_kv, qlast + off + 1);
+  }
+  const int ntiles = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
+
+  f32x16_t oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16_t{0};
+  float m = kNegInf;  // running max, in units of log2 (scores * scale * log2 e)
+  float l = 0.f;      // this half-wave's part of the running denominator
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int kv0 = t * kBN;
+    // ---- stage K and V (row-major, zero past N_kv) into LDS
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
+#pragma unroll
+    for (int c = tid; c < kBN * CPR; c += kThreads) {
+      const int r = c / CPR, cc = c % CPR;
+      u32x4_t kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (kv0 + r < N_kv) {
+        kv = *(const u32x4_t*)(Kh + (int64_t)(kv0 + r) * D + cc * 8);
+        vv = *(const u32x4_t*)(Vh + (int64_t)(kv0 + r) * D + cc * 8);
+      }
+      *(u32x4_t*)(sK + r * KST + cc * 8) = kv;
+      *(u32x4_t*)(sV + r * VST + cc * 8) = vv;
+    }
+    __syncthreads();
+
+    // wavefront-uniform: does this tile hold any key visible to this wavefront?
+    const bool live = !CAUSAL || kv0 <= q0 + 31 + off;
+    if (live) {
+      // ---- S^T = K Q^T for two 32-key blocks
+      f32x16_t s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16_t{0};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const u32x4_t a = *(const u32x4_t*)(sK + (kb * 32 + lr) * KST + 16 * st + 8 * lh);
+          s[kb] = TT::mfma32(a, qreg[st], s[kb]);
+        }
+      }
+      // ---- scale, mask (tail and causal diagonal tiles only), row max
+      const bool need_mask = (kv0 + kBN > N_kv) || (CAUSAL && kv0 + kBN - 1 > q0 + off);
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[kb][r] * scale_log2;
+          if (need_mask) {
+            const int kv = kv0 + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            if (kv >= N_kv || (CAUSAL && kv > qrow + off)) x = kNegInf;
+          }
+          s[kb][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m, mx);
+      const float m_ref = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m - m_ref);  // 0 when m is still -inf
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+
+      // ---- P = exp2(S - m), packed to 16-bit as the B operand of the PV MFMA
+      uint32_t pk[2][8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(s[kb][r] - m_ref);
+          const float p1 = fast_exp2(s[kb][r + 1] - m_ref);
+          l += p0 + p1;
+          pk[kb][r >> 1] = TT::pack2(p0, p1);
+        }
+      }
+
+      // ---- O^T += V^T P^T, four 16-key steps
+      const int g = lane >> 4;   // 16-lane group
+      const int gi = lane & 15;  // lane within group
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const u32x4_t bop = {pk[t4 >> 1][(t4 & 1) * 4 + 0], pk[t4 >> 1][(t4 & 1) * 4 + 1],
+                             pk[t4 >> 1][(t4 & 1) * 4 + 2], pk[t4 >> 1][(t4 & 1) * 4 + 3]};
+        // key rows for this lane's K-slots: 16*t4 + 4*lh + {0..3}, then +8
+        const int krow = 16 * t4 + 4 * (g >> 1) + (gi >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int dcol = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
+          const u32x2_t lo = lds_read_tr16(sV + krow * VST + dcol);
+          const u32x2_t hi = lds_read_tr16(sV + (krow + 8) * VST + dcol);
+          const u32x4_t aop = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[db] = TT::mfma32(aop, bop, oacc[db]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: combine half-wave denominators, normalise, store
+  l += xor32(l);
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  if (qrow < N_q) {
+    uint16_t* Orow = O + ((int64_t)b * H_q + h) * (int64_t)N_q * D + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = db * 32 + 8 * rg + 4 * lh;
+        u32x2_t w = {TT::pack2(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv),
+                     TT::pack2(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv)};
+        *(u32x2_t*)(Orow + d) = w;
+      }
+    }
+    if (LSE != nullptr && lh == 0) {
+      LSE[((int64_t)b * H_q + h) * N_q + qrow] = (l > 0.f) ? (m + log2f(l)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 inputs
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void prefill32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
+    float scale_log2, int nqb) {
+  constexpr int BN = 32;
+  constexpr int ST = D + 4;  // LDS row stride (floats)
+  constexpr int KH = D / 2;  // K-slots per lane half
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(16))) float sK[BN * ST];
+  __shared__ __attribute__((aligned(16))) float sV[BN * ST];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int qb = CAUSAL ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / (H_q / H_kv);
+  const float* Qh = Q + ((int64_t)b * H_q + h) * (int64_t)N_q * D;
+  const float* Kh = K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
+  const float* Vh = V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
+  const int q0 = qb * kBM + wave * 32, qrow = q0 + lr, off = N_kv - N_q;
+
+  // K index of the score contraction: lane half lh, step s <-> d = lh*D/2 + s
+  float qreg[KH];
+#pragma unroll
+  for (int s = 0; s < KH; s += 4) {
+    f32x4_t v = (qrow < N_q) ? *(const f32x4_t*)(Qh + (int64_t)qrow * D + lh * KH + s)
+                             : f32x4_t{0, 0, 0, 0};
+    qreg[s] = v[0]; qreg[s + 1] = v[1]; qreg[s + 2] = v[2]; qreg[s + 3] = v[3];
+  }
+  int kv_end = N_kv;
+  if (CAUSAL) kv_end = min(N_kv, min(qb * kBM + kBM - 1, N_q - 1) + off + 1);
+  const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+
+  f32x16_t oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16_t{0};
+  float m = kNegInf, l = 0.f;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int kv0 = t * BN;
+    constexpr int CPR = D / 4;
+    for (int c = tid; c < BN * CPR; c += kThreads) {
+      const int r = c / CPR, cc = c % CPR;
+      f32x4_t kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (kv0 + r < N_kv) {
+        kv = *(const f32x4_t*)(Kh + (int64_t)(kv0 + r) * D + cc * 4);
+        vv = *(const f32x4_t*)(Vh + (int64_t)(kv0 + r) * D + cc * 4);
+      }
+      *(f32x4_t*)(sK + r * ST + cc * 4) = kv;
+      *(f32x4_t*)(sV + r * ST + cc * 4) = vv;
+    }
+    __syncthreads();
+    const bool live = !CAUSAL || kv0 <= q0 + 31 + off;
+    if (live) {
+      f32x16_t s = f32x16_t{0};
+#pragma unroll
+      for (int st = 0; st < KH; ++st) {
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(sK[lr * ST + lh * KH + st], qreg[st], s, 0, 0, 0);
+      }
+      const bool need_mask = (kv0 + BN > N_kv) || (CAUSAL && kv0 + BN - 1 > q0 + off);
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[r] * scale_log2;
+        if (need_mask) {
+          const int kv = kv0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          if (kv >= N_kv || (CAUSAL && kv > qrow + off)) x = kNegInf;
+        }
+        s[r] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m, mx);
+      const float m_ref = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m - m_ref);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(s[r] - m_ref);
+        l += p;
+        // K-slot of this step: half lh carries key 8*(r/4) + 4*lh + r%4
+        const int kr = 8 * (r >> 2) + 4 * lh + (r & 3);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(sV[kr * ST + db * 32 + lr], p, oacc[db], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  l += xor32(l);
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  if (qrow < N_q) {
+    float* Orow = O + ((int64_t)b * H_q + h) * (int64_t)N_q * D + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = db * 32 + 8 * rg + 4 * lh;
+        f32x4_t w = {oacc[db][4 * rg] * inv, oacc[db][4 * rg + 1] * inv, oacc[db][4 * rg + 2] * inv,
+                     oacc[db][4 * rg + 3] * inv};
+        *(f32x4_t*)(Orow + d) = w;
+      }
+    }
+    if (LSE != nullptr && lh == 0) {
+      LSE[((int64_t)b * H_q + h) * N_q + qrow] = (l > 0.f) ? (m + log2f(l)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+template <class TT, int D>
+hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
+  const int nqb = (a.N_q + kBM - 1) / kBM;
+  dim3 grid(nqb, a.H_q, a.B);
+  const float sl2 = a.scale * kLog2e;
+  auto q = (const uint16_t*)a.q;
+  auto k = (const uint16_t*)a.k;
+  auto v = (const uint16_t*)a.v;
+  auto o = (uint16_t*)a.o;
+  if (a.causal)
+    hipLaunchKernelGGL((prefill16_kernel<TT, D, true>), grid, dim3(kThreads), 0, st, q, k, v, o,
+                       a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb);
+  else
+    hipLaunchKernelGGL((prefill16_kernel<TT, D, false>), grid, dim3(kThreads), 0, st, q, k, v, o,
+                       a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch32(const PrefillArgs& a, hipStream_t st) {
+  const int nqb = (a.N_q + kBM - 1) / kBM;
+  dim3 grid(nqb, a.H_q, a.B);
+  const float sl2 = a.scale * kLog2e;
+  auto q = (const float*)a.q;
+  auto k = (const float*)a.k;
+  auto v = (const float*)a.v;
+  auto o = (float*)a.o;
+  if (a.causal)
+    hipLaunchKernelGGL((prefill32_kernel<D, true>), grid, dim3(kThreads), 0, st, q, k, v, o, a.lse,
+                       a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb);
+  else
+    hipLaunchKernelGGL((prefill32_kernel<D, false>), grid, dim3(kThreads), 0, st, q, k, v, o, a.lse,
+                       a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+  switch (a.dtype) {
+    case kDtypeBF16:
+      return a.d == 64 ? launch16<BF16, 64>(a, st) : launch16<BF16, 128>(a, st);
+    case kDtypeF16:
+      return a.d == 64 ? launch16<F16, 64>(a, st) : launch16<F16, 128>(a, st);
+    default:
+      return a.d == 64 ? launch32<64>(a, st) : launch32<128>(a, st);
+  }
+}
+
+}  // namespace attn

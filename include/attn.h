@@ -1,0 +1,109 @@
+/*
+ * Exact scaled-dot-product attention for AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * Computes O = softmax(scale * Q K^T) V block by block with the online-softmax
+ * statistics (running max m, denominator l, un-normalised output u, rescaled by
+ * exp(m - m') when a block raises the max, output u / l), so the score matrix is
+ * never written to device memory. Definitions: auturnal.com transformer-attention
+ * guide (v10), section 2 (the formula) and section 8 (the blockwise statistics);
+ * marketmaker.cc "Flash Attention und die Frage nach der Sequenzlaenge", sections
+ * on the algorithm, the online-softmax recurrence and causal masking.
+ *
+ * Conventions shared by every entry point:
+ *  - Layout. Q and O are [B, H_q, N_q, d]; K and V are [B, H_kv, N_kv, d]; all
+ *    contiguous row-major, all of one element type `dtype` (O has the input
+ *    type). LSE, when requested, is float32 [B, H_q, N_q] in natural log
+ *    (lse = m + ln l). Tensors are [batch, heads, seq, head_dim] as in the
+ *    papanda925.com survey's standard-attention pseudo-code.
+ *  - Grouped-query attention: H_q must be a multiple of H_kv; query head h reads
+ *    KV head h / (H_q / H_kv) (code-journey.com attention co-design summary,
+ *    "Group Size(G)": G query heads share one KV head).
+ *  - Causal masking uses bottom-right alignment: query i sees key j iff
+ *    j <= i + (n - N_q), n being the number of valid keys. For N_q == n this is
+ *    j <= i; a single decode query sees every valid key. Key blocks entirely in
+ *    a query block's future are skipped.
+ *  - Rows with no visible key produce O = 0 and LSE = -inf.
+ *  - Memory. All pointers are device pointers owned by the caller. The library
+ *    never allocates, frees or synchronises: it enqueues work on `stream` (a
+ *    hipStream_t; NULL is the default stream) and returns. Inputs are read only.
+ *    O and LSE must not overlap any input.
+ *  - Errors. Arguments are checked before anything is enqueued; on a nonzero
+ *    status nothing was enqueued, except ATTN_ERR_LAUNCH (the HIP launch
+ *    itself failed). There is no fallback path: inputs the kernels do not
+ *    cover are rejected with ATTN_ERR_UNSUPPORTED.
+ *  - Supported: dtype ATTN_F32, ATTN_F16, ATTN_BF16 (decode: F16 and BF16);
+ *    d in {64, 128}; gfx950 devices only.
+ */
+#ifndef EXACT_ATTENTION_ATTN_H_
+#define EXACT_ATTENTION_ATTN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* negative or inconsistent sizes, or sizes beyond the grid limits */
+  ATTN_ERR_GQA = 3,         /* H_q is not a positive multiple of H_kv */
+  ATTN_ERR_UNSUPPORTED = 4, /* dtype, head dim, N_q or device not covered by the kernels */
+  ATTN_ERR_WORKSPACE = 5,   /* decode workspace missing or smaller than required */
+  ATTN_ERR_LAUNCH = 6,      /* the HIP launch reported an error */
+  ATTN_ERR_NO_DEVICE = 7,   /* no HIP device is visible */
+  ATTN_ERR_ALIAS = 8,       /* an output overlaps an input */
+  ATTN_ERR_VALUE = 9        /* scale is not finite */
+} attn_status_t;
+
+/*
+ * Prefill (and general) forward: every query row of Q attends to the N_kv keys.
+ *   q [B,H_q,N_q,d], k/v [B,H_kv,N_kv,d], o [B,H_q,N_q,d] (same dtype);
+ *   lse: float32 [B,H_q,N_q] or NULL;
+ *   causal: 0 or 1 (bottom-right alignment); scale: usually 1/sqrt(d).
+ * Empty problems (B, N_q or H_q zero) return ATTN_OK and enqueue nothing.
+ * Work: 4*d FLOP per visible (query, key) pair per query head, on MFMA.
+ */
+int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H_q, int H_kv, int N_q, int N_kv, int d, int causal, float scale,
+                     int dtype, void* stream);
+
+/*
+ * Bytes of device workspace attn_decode_fwd needs for these sizes (0 if the
+ * sizes are invalid). The split of the KV sequence is a pure function of
+ * (B, H_q, H_kv, N_kv, d), so the same sizes always need the same workspace.
+ */
+size_t attn_decode_workspace_size(int B, int H_q, int H_kv, int N_q, int N_kv, int d, int dtype);
+
+/*
+ * Decode forward (split-KV, grouped-query): one query token per request against
+ * a KV cache of capacity N_kv, of which the first kv_lens[b] positions are valid.
+ * The KV sequence is split into chunks; each chunk produces partial (m, l, u) per
+ * query head, which a second kernel merges by log-sum-exp weights exp(m_s - m)
+ * (the online-softmax rescaling of the guide's section 8 applied across chunks).
+ *   q [B,H_q,1,d], k_cache/v_cache [B,H_kv,N_kv,d], o [B,H_q,1,d];
+ *   kv_lens: device int32 [B] or NULL (all N_kv); values are clamped to [0, N_kv];
+ *   lse: float32 [B,H_q,1] or NULL; N_q must be 1 (else ATTN_ERR_UNSUPPORTED);
+ *   causal is accepted and has no effect for a single query (it sees all keys);
+ *   workspace: device memory of at least attn_decode_workspace_size(...) bytes,
+ *   owned by the caller, overwritten by the call (no initialisation needed).
+ * Work: 2 * kv_lens[b] * H_kv * d * sizeof(dtype) bytes of K and V read.
+ */
+int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
+                    void* o, float* lse, int B, int H_q, int H_kv, int N_q, int N_kv, int d,
+                    int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_ATTN_H_ */

@@ -1,0 +1,107 @@
+"""GPU parity of attn_decode_fwd (split-KV GQA decode + LSE merge) against the
+float64 oracle (MI355X only)."""
+import math
+import os
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as A
+import exact_attention_31_amd as E
+from gpu_helpers import TOL_LSE, TOL_O, check_lse, device_tensor, max_abs_err, to_device, to_host64
+from oracle import attention_head_rows, attention_ref
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _decode_case(B, Hq, Hkv, Nkv, d, dtype, lens, seed, poison=False):
+    _announce(f"decode B={B} Hq={Hq} Hkv={Hkv} Nkv={Nkv} d={d} {dtype} lens={None if lens is None else list(lens)[:6]}")
+    q = A.random_tensor((B, Hq, 1, d), seed * 3, dtype)
+    k = A.random_tensor((B, Hkv, Nkv, d), seed * 3 + 1, dtype)
+    v = A.random_tensor((B, Hkv, Nkv, d), seed * 3 + 2, dtype)
+    kd, vd = to_device(k, dtype), to_device(v, dtype)
+    lens_d = None
+    if lens is not None:
+        lens = np.asarray(lens, dtype=np.int32)
+        lens_d = torch.from_numpy(lens).cuda()
+        if poison:   # positions past each request's length must never be read
+            for b, n in enumerate(lens):
+                kd[b, :, n:] = float("nan")
+                vd[b, :, n:] = float("nan")
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = E.attn_decode_fwd(to_device(q, dtype), kd, vd, kv_lens=lens_d, scale=scale,
+                               return_lse=True)
+    torch.cuda.synchronize()
+    oref, lref = attention_ref(q, k, v, False, scale, kv_lens=lens)
+    got = to_host64(o)
+    assert np.all(np.isfinite(got))
+    err = max_abs_err(got, oref)
+    assert err <= TOL_O[dtype], f"max |err| {err}"
+    check_lse(lse.cpu().numpy().astype(np.float64), lref, TOL_LSE[dtype])
+
+
+CASES = [
+    # B, Hq, Hkv, Nkv, d, lens
+    (1, 8, 1, 1, 128, None), (2, 8, 1, 100, 128, None), (3, 32, 4, 1000, 128, [1000, 1, 517]),
+    (2, 4, 4, 300, 64, [0, 300]), (2, 16, 1, 2049, 128, [2049, 1234]), (1, 32, 1, 700, 64, None),
+    (4, 24, 2, 5000, 128, [5000, 4097, 128, 129]), (2, 2, 2, 130, 128, None),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c[:5])))
+def test_decode_small_matches_oracle(case, dtype):
+    *shape, lens = case
+    _decode_case(*shape, dtype, lens, seed=zlib.crc32(repr((case, dtype)).encode()) % 10000)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_decode_never_reads_past_kv_lens(dtype):
+    _decode_case(3, 16, 2, 3000, 128, dtype, [2999, 5, 1500], seed=77, poison=True)
+
+
+def test_decode_causal_flag_is_a_no_op_for_one_query():
+    q = to_device(A.random_tensor((2, 8, 1, 128), 5, "bf16"), "bf16")
+    k = to_device(A.random_tensor((2, 1, 333, 128), 6, "bf16"), "bf16")
+    v = to_device(A.random_tensor((2, 1, 333, 128), 7, "bf16"), "bf16")
+    o1 = E.attn_decode_fwd(q, k, v, causal=False)
+    o2 = E.attn_decode_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("ragged", [False, True])
+def test_decode_config5_full_size(ragged):
+    """Config 5 (B=64, H_q=32, H_kv=4, KV 32768, bf16), every query head checked."""
+    cfg = A.CONFIGS[6 if ragged else 5]
+    _announce(cfg.name)
+    lens = A.ragged_lengths(cfg) if ragged else np.full(cfg.B, cfg.N_kv, np.int32)
+    kv_keep = [(b, g) for b in range(cfg.B) for g in range(cfg.H_kv)]
+    q, qk = device_tensor(cfg, "q", keep=[(b, h) for b in range(cfg.B) for h in range(cfg.H_q)])
+    k, kk = device_tensor(cfg, "k", keep=kv_keep)
+    v, vk = device_tensor(cfg, "v", keep=kv_keep)
+    lens_d = torch.from_numpy(lens).cuda()
+    o, lse = E.attn_decode_fwd(q, k, v, kv_lens=lens_d, scale=cfg.scale, return_lse=True)
+    torch.cuda.synchronize()
+    og = to_host64(o)
+    lg = lse.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for b in range(cfg.B):
+        for h in range(cfg.H_q):
+            g = h // cfg.G
+            oref, lref = attention_head_rows(qk[(b, h)], [0], 1, kk[(b, g)], vk[(b, g)], False,
+                                             cfg.scale, n=int(lens[b]))
+            err = max_abs_err(og[b, h], oref)
+            worst = max(worst, err)
+            assert err <= TOL_O[cfg.dtype], f"(b={b}, h={h}) max |err| {err}"
+            check_lse(lg[b, h], lref, TOL_LSE[cfg.dtype])
+    print(f"{cfg.name}: worst max|err| = {worst:.3e}", flush=True)
