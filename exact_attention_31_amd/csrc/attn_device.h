@@ -70,6 +70,35 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Exchange with the lane 32 positions away (the other half of the wavefront).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
+// Cross-half reductions without LDS: v_permlane32_swap(x, x) leaves, in every
+// lane i, the values of lanes i % 32 and i % 32 + 32 in its two results.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// True in every lane if `p` holds in any lane of the wavefront (uniform branch).
+__device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
+
+// Raw buffer resource over [base, base + nbytes): loads past the end return
+// zeros and stores past the end are dropped, with no branches in the kernel.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+}
+__device__ __forceinline__ void buffer_store8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)byte_off, 0, 0);
+}
+
 // LDS transposing read (gfx950 ds_read_b64_tr_b16). Within each group of 16
 // lanes, lane i addresses 4 consecutive 16-bit elements of row i/4, columns
 // 4*(i%4)..+3, of a 4 x 16 block; lane i receives column i of that block, i.e.

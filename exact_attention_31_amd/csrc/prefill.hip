@@ -44,6 +44,12 @@ template <int D> struct Lds16 {
   static constexpr int kV = D + 16;
 };
 
+// Rescale threshold (log2 units): a row's reference maximum is only raised when
+// a block's maximum exceeds it by more than this, so most blocks skip the
+// rescale of l and u. Probabilities then stay below 2^8, and l and u keep one
+// common reference point, so u / l is unchanged.
+constexpr float kLazyRescale = 8.f;
+
 template <class TT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -53,8 +59,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(
   constexpr int VST = Lds16<D>::kV;
   constexpr int KS = D / 16;   // k-steps of the score MFMA
   constexpr int DB = D / 32;   // 32-wide blocks of the output
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBN * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kBN * VST];
+  constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
+  constexpr int LPT = kBN * CPR / kThreads;  // 16-byte loads per thread per tile, per tensor
+  static_assert(LPT * kThreads == kBN * CPR, "tile load must split evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * KST];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBN * VST];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -67,20 +76,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(
   const int b = blockIdx.z;
   const int hk = h / (H_q / H_kv);
 
-  const uint16_t* Qh = Q + ((int64_t)b * H_q + h) * (int64_t)N_q * D;
-  const uint16_t* Kh = K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
-  const uint16_t* Vh = V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
+  const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
+  const uint32_t head_kv_bytes = (uint32_t)N_kv * D * 2;
+  const auto rQ = buffer_rsrc(Q + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
+  const auto rK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
+  const auto rV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
 
   const int q0 = qb * kBM + wave * 32;  // first row of this wavefront
   const int qrow = q0 + lr;             // this lane's row
   const int off = N_kv - N_q;           // bottom-right causal alignment
+  // keys below `lim` are visible to this lane's row
+  const int lim = CAUSAL ? min(N_kv, max(qrow + off + 1, 0)) : N_kv;
 
+  // Q^T operand: lane holds row qrow, d = 16*s + 8*lh + 0..7 (rows past N_q read as 0)
   u32x4_t qreg[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    qreg[s] = (qrow < N_q) ? *(const u32x4_t*)(Qh + (int64_t)qrow * D + 16 * s + 8 * lh)
-                           : u32x4_t{0, 0, 0, 0};
-  }
+  for (int s = 0; s < KS; ++s) qreg[s] = buffer_load16(rQ, (uint32_t)(qrow * D + 16 * s + 8 * lh) * 2);
 
   int kv_end = N_kv;
   if (CAUSAL) {
@@ -89,121 +100,142 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(
   }
   const int ntiles = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
 
+  // this thread's share of each tile: chunk c = tid + kThreads*i -> row c / CPR, column c % CPR
+  uint32_t ld_off[LPT];
+  int st_k[LPT], st_v[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int c = tid + kThreads * i;
+    const int r = c / CPR, cc = c % CPR;
+    ld_off[i] = (uint32_t)(r * D + cc * 8) * 2;
+    st_k[i] = r * KST + cc * 8;
+    st_v[i] = r * VST + cc * 8;
+  }
+  u32x4_t kbuf[LPT], vbuf[LPT];
+  auto load_tile = [&](int t) {
+    const uint32_t base = (uint32_t)(t * kBN) * D * 2;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      kbuf[i] = buffer_load16(rK, base + ld_off[i]);
+      vbuf[i] = buffer_load16(rV, base + ld_off[i]);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      *(u32x4_t*)(&sK[buf][st_k[i]]) = kbuf[i];
+      *(u32x4_t*)(&sV[buf][st_v[i]]) = vbuf[i];
+    }
+  };
+
   f32x16_t oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16_t{0};
-  float m = kNegInf;  // running max, in units of log2 (scores * scale * log2 e)
-  float l = 0.f;      // this half-wave's part of the running denominator
+  float m = kNegInf;  // reference maximum, in units of log2 (scores * scale * log2 e)
+  float l = 0.f;      // this half-wave's part of the denominator
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);  // in flight during this tile's math
     const int kv0 = t * kBN;
-    // ---- stage K and V (row-major, zero past N_kv) into LDS
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
-#pragma unroll
-    for (int c = tid; c < kBN * CPR; c += kThreads) {
-      const int r = c / CPR, cc = c % CPR;
-      u32x4_t kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (kv0 + r < N_kv) {
-        kv = *(const u32x4_t*)(Kh + (int64_t)(kv0 + r) * D + cc * 8);
-        vv = *(const u32x4_t*)(Vh + (int64_t)(kv0 + r) * D + cc * 8);
-      }
-      *(u32x4_t*)(sK + r * KST + cc * 8) = kv;
-      *(u32x4_t*)(sV + r * VST + cc * 8) = vv;
-    }
-    __syncthreads();
-
     // wavefront-uniform: does this tile hold any key visible to this wavefront?
     const bool live = !CAUSAL || kv0 <= q0 + 31 + off;
     if (live) {
+      const uint16_t* tK = sK[buf];
+      const uint16_t* tV = sV[buf];
       // ---- S^T = K Q^T for two 32-key blocks
-      f32x16_t s[2];
+      f32x16_t s0 = f32x16_t{0}, s1 = f32x16_t{0};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16_t{0};
-#pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          const u32x4_t a = *(const u32x4_t*)(sK + (kb * 32 + lr) * KST + 16 * st + 8 * lh);
-          s[kb] = TT::mfma32(a, qreg[st], s[kb]);
-        }
+      for (int st = 0; st < KS; ++st) {
+        const u32x4_t a0 = *(const u32x4_t*)(tK + lr * KST + 16 * st + 8 * lh);
+        const u32x4_t a1 = *(const u32x4_t*)(tK + (32 + lr) * KST + 16 * st + 8 * lh);
+        s0 = TT::mfma32(a0, qreg[st], s0);
+        s1 = TT::mfma32(a1, qreg[st], s1);
       }
-      // ---- scale, mask (tail and causal diagonal tiles only), row max
+      // ---- mask (tail and causal diagonal tiles only), branch-free per element
       const bool need_mask = (kv0 + kBN > N_kv) || (CAUSAL && kv0 + kBN - 1 > q0 + off);
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      if (need_mask) {
+        const int kvb = kv0 + 4 * lh;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r] * scale_log2;
-          if (need_mask) {
-            const int kv = kv0 + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            if (kv >= N_kv || (CAUSAL && kv > qrow + off)) x = kNegInf;
-          }
-          s[kb][r] = x;
-          mx = fmaxf(mx, x);
+          const int kv = kvb + 8 * (r >> 2) + (r & 3);
+          s0[r] = (kv < lim) ? s0[r] : kNegInf;
+          s1[r] = (kv + 32 < lim) ? s1[r] : kNegInf;
         }
       }
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m, mx);
-      const float m_ref = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_ref);  // 0 when m is still -inf
-      m = m_new;
-      l *= alpha;
+      // ---- row max of the raw scores (scale > 0 commutes with max)
+      float mx = kNegInf;
 #pragma unroll
-      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-
-      // ---- P = exp2(S - m), packed to 16-bit as the B operand of the PV MFMA
-      uint32_t pk[2][8];
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      const float mxs = half_max(mx) * scale_log2;
+      // The branch is wavefront-uniform, but each lane moves only its own
+      // reference (alpha = 1 is an exact multiply), so a row's arithmetic never
+      // depends on the other rows of the wavefront.
+      const bool need = mxs > m + kLazyRescale;
+      if (wave_any(need)) {
+        const float alpha = need ? ((m == kNegInf) ? 0.f : fast_exp2(m - mxs)) : 1.f;
+        m = need ? mxs : m;
+        l *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(s[kb][r] - m_ref);
-          const float p1 = fast_exp2(s[kb][r + 1] - m_ref);
-          l += p0 + p1;
-          pk[kb][r >> 1] = TT::pack2(p0, p1);
-        }
+        for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
       }
-
-      // ---- O^T += V^T P^T, four 16-key steps
+      const float nm = (m == kNegInf) ? 0.f : -m;
+      // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
+      uint32_t pk[16];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s0[r], scale_log2, nm));
+        const float p1 = fast_exp2(__builtin_fmaf(s0[r + 1], scale_log2, nm));
+        const float p2 = fast_exp2(__builtin_fmaf(s1[r], scale_log2, nm));
+        const float p3 = fast_exp2(__builtin_fmaf(s1[r + 1], scale_log2, nm));
+        l += (p0 + p1) + (p2 + p3);
+        pk[r >> 1] = TT::pack2(p0, p1);
+        pk[8 + (r >> 1)] = TT::pack2(p2, p3);
+      }
+      // ---- O^T += V^T P^T, four 16-key steps; V^T through the transposing LDS read
       const int g = lane >> 4;   // 16-lane group
       const int gi = lane & 15;  // lane within group
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        const u32x4_t bop = {pk[t4 >> 1][(t4 & 1) * 4 + 0], pk[t4 >> 1][(t4 & 1) * 4 + 1],
-                             pk[t4 >> 1][(t4 & 1) * 4 + 2], pk[t4 >> 1][(t4 & 1) * 4 + 3]};
-        // key rows for this lane's K-slots: 16*t4 + 4*lh + {0..3}, then +8
+        const u32x4_t bop = {pk[4 * t4 + 0], pk[4 * t4 + 1], pk[4 * t4 + 2], pk[4 * t4 + 3]};
+        // key rows of this lane's K-slots: 16*t4 + 4*lh + {0..3}, then the same + 8
         const int krow = 16 * t4 + 4 * (g >> 1) + (gi >> 2);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int dcol = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
-          const u32x2_t lo = lds_read_tr16(sV + krow * VST + dcol);
-          const u32x2_t hi = lds_read_tr16(sV + (krow + 8) * VST + dcol);
+          const u32x2_t lo = lds_read_tr16(tV + krow * VST + dcol);
+          const u32x2_t hi = lds_read_tr16(tV + (krow + 8) * VST + dcol);
           const u32x4_t aop = {lo[0], lo[1], hi[0], hi[1]};
           oacc[db] = TT::mfma32(aop, bop, oacc[db]);
         }
       }
     }
+    if (t + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue: combine half-wave denominators, normalise, store
-  l += xor32(l);
+  // ---- epilogue: combine half-wave denominators, normalise, store (rows past N_q dropped)
+  l = half_sum(l);
   const float inv = (l > 0.f) ? 1.f / l : 0.f;
-  if (qrow < N_q) {
-    uint16_t* Orow = O + ((int64_t)b * H_q + h) * (int64_t)N_q * D + (int64_t)qrow * D;
+  const auto rO = buffer_rsrc(O + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+  for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d = db * 32 + 8 * rg + 4 * lh;
-        u32x2_t w = {TT::pack2(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv),
-                     TT::pack2(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv)};
-        *(u32x2_t*)(Orow + d) = w;
-      }
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d = db * 32 + 8 * rg + 4 * lh;
+      const u32x2_t w = {TT::pack2(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv),
+                         TT::pack2(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv)};
+      buffer_store8(rO, (uint32_t)(qrow * D + d) * 2, w);
     }
-    if (LSE != nullptr && lh == 0) {
-      LSE[((int64_t)b * H_q + h) * N_q + qrow] = (l > 0.f) ? (m + log2f(l)) * kLn2 : kNegInf;
-    }
+  }
+  if (LSE != nullptr && lh == 0 && qrow < N_q) {
+    LSE[((int64_t)b * H_q + h) * N_q + qrow] = (l > 0.f) ? (m + log2f(l)) * kLn2 : kNegInf;
   }
 }
 
