@@ -29,16 +29,26 @@ constexpr int kWaveKeys = 32;            // keys per wavefront step
 constexpr int kStepKeys = 4 * kWaveKeys; // keys per workgroup step
 constexpr int kQCols = 16;               // query heads per workgroup (MFMA N)
 
+// Orders this wavefront's LDS writes before its later LDS reads (the lanes of a
+// wavefront exchange V rows through LDS; no other wavefront touches them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <class TT, int D>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int* __restrict__ kv_lens, float* __restrict__ part_u, float* __restrict__ part_ml,
     int H_q, int H_kv, int N_kv, int splits, int chunk, float scale_log2) {
   constexpr int VST = D + 16;       // LDS row stride of the staged V rows
   constexpr int KS = D / 32;        // k-steps of the score MFMA
   constexpr int DB = D / 16;        // 16-wide output blocks
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int VL = kWaveKeys * CPR / 64;        // V loads per lane per step
   constexpr int kV = 4 * kWaveKeys * VST;          // V staging (elements)
-  constexpr int kComb = 4 * kQCols * (D + 2) * 2;  // combine area, in 16-bit units
+  constexpr int kComb = 4 * kQCols * (2 + D + 1) * 2;  // combine area, in 16-bit units
   constexpr int kLds = kV > kComb ? kV : kComb;
   __shared__ __attribute__((aligned(16))) uint16_t smem[kLds];
 
@@ -57,20 +67,25 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const int start = split * chunk;
   if (start >= len) return;  // nothing in this split (its partial is never read)
   const int end = min(start + chunk, len);
+  // each wavefront takes a contiguous quarter of the chunk
+  const int wq = chunk / 4;
+  const int wbeg = min(start + wave * wq, end);
+  const int wend = min(wbeg + wq, end);
+  const int nsteps = (wend - wbeg + kWaveKeys - 1) / kWaveKeys;
 
-  const uint16_t* Kh = K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
-  const uint16_t* Vh = V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
+  // rows past the request's length read as zeros
+  const uint32_t valid_bytes = (uint32_t)len * D * 2;
+  const auto rK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, valid_bytes);
+  const auto rV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, valid_bytes);
   const int hq0 = hk * G + qg * kQCols;       // first query head of this group
   const int ncols = min(kQCols, G - qg * kQCols);
 
   // Q^T operand: column c16 = query head hq0 + c16, K-slots d = 32*st + 8*g + 0..7
   u32x4_t qreg[KS];
   {
-    const bool ok = c16 < ncols;
-    const uint16_t* Qh = Q + ((int64_t)b * H_q + hq0 + c16) * D;
+    const auto rQ = buffer_rsrc(Q + ((int64_t)b * H_q + hq0) * D, (uint32_t)ncols * D * 2);
 #pragma unroll
-    for (int st = 0; st < KS; ++st)
-      qreg[st] = ok ? *(const u32x4_t*)(Qh + 32 * st + 8 * g) : u32x4_t{0, 0, 0, 0};
+    for (int st = 0; st < KS; ++st) qreg[st] = buffer_load16(rQ, (uint32_t)(c16 * D + 32 * st + 8 * g) * 2);
   }
 
   f32x4_t oacc[DB];
@@ -79,49 +94,51 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   float m = kNegInf, l = 0.f;
   uint16_t* sV = smem + wave * kWaveKeys * VST;
 
-  for (int t0 = start; t0 < end; t0 += kStepKeys) {
-    const int w0 = t0 + wave * kWaveKeys;  // this wavefront's first key
-    // ---- stage this wavefront's 32 V rows in LDS (zero past the end)
-    constexpr int CPR = D / 8;
+  // K rows feed the A operand directly: key = w0 + 16*kb + c16, d = 32*st + 8*g
+  // V rows: lane takes chunk c = lane + 64*i -> row c / CPR, column c % CPR
+  u32x4_t ka[2][2][KS], va[2][VL];
+  auto issue = [&](int w0, u32x4_t (&kk)[2][KS], u32x4_t (&vv)[VL]) {
 #pragma unroll
-    for (int c = lane; c < kWaveKeys * CPR; c += 64) {
-      const int r = c / CPR, cc = c % CPR;
-      u32x4_t vv = {0, 0, 0, 0};
-      if (w0 + r < end) vv = *(const u32x4_t*)(Vh + (int64_t)(w0 + r) * D + cc * 8);
-      *(u32x4_t*)(sV + r * VST + cc * 8) = vv;
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < KS; ++st)
+        kk[kb][st] = buffer_load16(rK, (uint32_t)((w0 + kb * 16 + c16) * D + 32 * st + 8 * g) * 2);
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int c = lane + 64 * i;
+      vv[i] = buffer_load16(rV, (uint32_t)((w0 + c / CPR) * D + (c % CPR) * 8) * 2);
     }
-    // ---- S^T = K Q^T for two 16-key blocks, K straight from HBM
+  };
+  auto step = [&](int w0, const u32x4_t (&kk)[2][KS], const u32x4_t (&vv)[VL]) {
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int c = lane + 64 * i;
+      *(u32x4_t*)(sV + (c / CPR) * VST + (c % CPR) * 8) = vv[i];
+    }
     f32x4_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int key = w0 + kb * 16 + c16;
-      u32x4_t a[KS];
-#pragma unroll
-      for (int st = 0; st < KS; ++st)
-        a[st] = (key < end) ? *(const u32x4_t*)(Kh + (int64_t)key * D + 32 * st + 8 * g)
-                            : u32x4_t{0, 0, 0, 0};
       s[kb] = f32x4_t{0, 0, 0, 0};
 #pragma unroll
-      for (int st = 0; st < KS; ++st) s[kb] = TT::mfma16(a[st], qreg[st], s[kb]);
+      for (int st = 0; st < KS; ++st) s[kb] = TT::mfma16(kk[kb][st], qreg[st], s[kb]);
     }
-    // ---- mask keys past the end, running max over the wavefront's 32 keys
+    // mask keys past this wavefront's range, running max over its 32 keys
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = w0 + kb * 16 + 4 * g + r;
-        const float x = (key < end) ? s[kb][r] * scale_log2 : kNegInf;
-        s[kb][r] = x;
-        mx = fmaxf(mx, x);
+        s[kb][r] = (key < wend) ? s[kb][r] : kNegInf;
+        mx = fmaxf(mx, s[kb][r]);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = half_max(mx) * scale_log2;
     const float m_new = fmaxf(m, mx);
-    const float m_ref = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_ref);
+    const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - m_new);
     m = m_new;
+    const float nm = (m == kNegInf) ? 0.f : -m;
     l *= alpha;
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
@@ -130,13 +147,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[kb][r] = fast_exp2(s[kb][r] - m_ref);
+        p[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, nm));
         l += p[kb][r];
       }
     // K-slots of lane group g: keys 4g+0..3 (block 0) then 16+4g+0..3 (block 1)
     const u32x4_t bop = {TT::pack2(p[0][0], p[0][1]), TT::pack2(p[0][2], p[0][3]),
                          TT::pack2(p[1][0], p[1][1]), TT::pack2(p[1][2], p[1][3])};
-    __syncthreads();  // V rows of this step are in LDS
+    wave_lds_sync();  // V rows of this step are in LDS
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int dcol = 16 * db + 4 * (c16 & 3);
@@ -145,15 +162,28 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       const u32x4_t aop = {lo[0], lo[1], hi[0], hi[1]};
       oacc[db] = TT::mfma16(aop, bop, oacc[db]);
     }
-    __syncthreads();  // before the next step overwrites the V rows
+    wave_lds_sync();  // reads done before the next step overwrites the rows
+  };
+
+  if (nsteps > 0) issue(wbeg, ka[0], va[0]);
+  for (int i = 0; i < nsteps; i += 2) {
+    const int w0 = wbeg + i * kWaveKeys;
+    if (i + 1 < nsteps) issue(w0 + kWaveKeys, ka[1], va[1]);
+    step(w0, ka[0], va[0]);
+    if (i + 1 < nsteps) {
+      if (i + 2 < nsteps) issue(w0 + 2 * kWaveKeys, ka[0], va[0]);
+      step(w0 + kWaveKeys, ka[1], va[1]);
+    }
   }
 
   // ---- combine the four wavefronts' partials through LDS
   l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = half_sum(l);
+  __syncthreads();  // all wavefronts are done with their V rows
   float* cm = (float*)smem;                 // [4][16] max
   float* cl = cm + 4 * kQCols;              // [4][16] denominator
-  float* cu = cl + 4 * kQCols;              // [4][16][D] output
+  float* cu = cl + 4 * kQCols;              // [4][16][D + 1] output (padded rows)
+  constexpr int UST = D + 1;
   if (g == 0) {
     cm[wave * kQCols + c16] = m;
     cl[wave * kQCols + c16] = l;
@@ -161,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) cu[(wave * kQCols + c16) * D + 16 * db + 4 * g + r] = oacc[db][r];
+    for (int r = 0; r < 4; ++r) cu[(wave * kQCols + c16) * UST + 16 * db + 4 * g + r] = oacc[db][r];
   __syncthreads();
   const int64_t row0 = ((int64_t)b * H_q + hq0) * splits + split;  // (b, hq0, split)
   for (int e = tid; e < ncols * D; e += kThreads) {
@@ -175,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     for (int w = 0; w < 4; ++w) {
       const float wt = fast_exp2(cm[w * kQCols + c] - Mref);
       L += wt * cl[w * kQCols + c];
-      U += wt * cu[(w * kQCols + c) * D + d];
+      U += wt * cu[(w * kQCols + c) * UST + d];
     }
     const int64_t row = row0 + (int64_t)c * splits;
     part_u[row * D + d] = U;
@@ -186,35 +216,57 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   }
 }
 
+// Merge of the split partials: out = sum_s w_s u_s / sum_s w_s l_s with
+// w_s = exp2(m_s - max_s m_s). One 64-lane wavefront per (request, query head);
+// lane i owns output column i (d = 64) or columns 2i, 2i+1 (d = 128).
 template <class TT, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(
+__global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part_u, const float* __restrict__ part_ml,
     const int* __restrict__ kv_lens, uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q,
-    int N_kv, int splits, int chunk) {
-  const int d = threadIdx.x;
-  const int h = blockIdx.x, b = blockIdx.y;
+    int N_kv, int splits, int chunk, int BH) {
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int PER = D / 64;  // columns per lane
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * H_q + h)
+  if (bh >= BH) return;
+  const int b = bh / H_q;
   int len = kv_lens ? kv_lens[b] : N_kv;
   len = min(max(len, 0), N_kv);
   const int ns = (len + chunk - 1) / chunk;
-  const int64_t row0 = ((int64_t)b * H_q + h) * splits;
+  const int64_t row0 = (int64_t)bh * splits;
   float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[(row0 + s) * 2]);
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, part_ml[(row0 + s) * 2]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   const float Mref = (M == kNegInf) ? 0.f : M;
-  float L = 0.f, U = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float wt = fast_exp2(part_ml[(row0 + s) * 2] - Mref);
-    L += wt * part_ml[(row0 + s) * 2 + 1];
-    U += wt * part_u[(row0 + s) * D + d];
+  float L = 0.f, U0 = 0.f, U1 = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int s = s0 + lane;
+    const float w = (s < ns) ? fast_exp2(part_ml[(row0 + s) * 2] - Mref) : 0.f;
+    L += (s < ns) ? w * part_ml[(row0 + s) * 2 + 1] : 0.f;
+    const int cnt = min(64, ns - s0);
+    for (int j = 0; j < cnt; ++j) {
+      const float wj = __shfl(w, j);
+      const float* u = part_u + (row0 + s0 + j) * D + PER * lane;
+      if constexpr (PER == 2) {
+        const float2 v = *(const float2*)u;
+        U0 += wj * v.x;
+        U1 += wj * v.y;
+      } else {
+        U0 += wj * u[0];
+      }
+    }
   }
-  const float o = (L > 0.f) ? U / L : 0.f;
-  // 16-bit store: pair adjacent lanes
-  const float o_hi = __shfl_down(o, 1);
-  if ((d & 1) == 0) {
-    *(uint32_t*)(O + ((int64_t)b * H_q + h) * D + d) = TT::pack2(o, o_hi);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+  uint16_t* out = O + (int64_t)bh * D + PER * lane;
+  if constexpr (PER == 2) {
+    *(uint32_t*)out = TT::pack2(U0 * inv, U1 * inv);
+  } else {
+    *out = (uint16_t)(TT::pack2(U0 * inv, 0.f) & 0xffffu);
   }
-  if (LSE != nullptr && d == 0) {
-    LSE[(int64_t)b * H_q + h] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
-  }
+  if (LSE != nullptr && lane == 0) LSE[bh] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
 template <class TT, int D>
@@ -228,8 +280,9 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
                      a.scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<TT, D>), dim3(a.H_q, a.B), dim3(D), 0, st, a.part_u,
-                     a.part_ml, a.kv_lens, (uint16_t*)a.o, a.lse, a.H_q, a.N_kv, a.splits, a.chunk);
+  const int BH = a.B * a.H_q;
+  hipLaunchKernelGGL((decode_merge_kernel<TT, D>), dim3((BH + 3) / 4), dim3(256), 0, st, a.part_u,
+                     a.part_ml, a.kv_lens, (uint16_t*)a.o, a.lse, a.H_q, a.N_kv, a.splits, a.chunk, BH);
   return hipGetLastError();
 }
 
