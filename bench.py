@@ -183,7 +183,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--all", action="store_true", help="also time configs 1, 3, 4 and ragged decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_ragged"], default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -210,6 +210,10 @@ def main(argv=None):
         print(f"# decode c5: {res['decode']['ms']:.3f} ms  {res['decode']['gb_per_s']:.0f} GB/s",
               file=sys.stderr, flush=True)
     extra = []
+    if args.only == "decode_ragged":
+        r = bench_decode(A.CONFIGS[6], args.steps, args.warmup, torch, E, ragged=True)
+        print(f"# decode c5 ragged: {r['ms']:.3f} ms  {r['gb_per_s']:.0f} GB/s", file=sys.stderr, flush=True)
+        res["decode"] = r
     if args.all:
         for cid in (1, 3, 4):
             r = bench_prefill(A.CONFIGS[cid], max(5, args.steps // 5) if cid == 4 else args.steps,

@@ -17,6 +17,8 @@
 // group's query heads form the B operand (padded to 16 columns). V rows are
 // staged in LDS and read back transposed (ds_read_b64_tr_b16) as the A operand
 // of O^T = V^T P^T, so each lane's accumulators belong to one query head.
+#include <stdlib.h>
+
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -245,15 +247,27 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float w = (s < ns) ? fast_exp2(part_ml[(row0 + s) * 2] - Mref) : 0.f;
     L += (s < ns) ? w * part_ml[(row0 + s) * 2 + 1] : 0.f;
     const int cnt = min(64, ns - s0);
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = __shfl(w, j);
-      const float* u = part_u + (row0 + s0 + j) * D + PER * lane;
-      if constexpr (PER == 2) {
-        const float2 v = *(const float2*)u;
-        U0 += wj * v.x;
-        U1 += wj * v.y;
-      } else {
-        U0 += wj * u[0];
+    const float* ub = part_u + (row0 + s0) * D + PER * lane;
+    // eight splits per batch: all loads issued before the accumulation
+    for (int j0 = 0; j0 < cnt; j0 += 8) {
+      float a0[8], a1[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int jj = min(j0 + j, cnt - 1);
+        if constexpr (PER == 2) {
+          const float2 v = *(const float2*)(ub + (int64_t)jj * D);
+          a0[j] = v.x;
+          a1[j] = v.y;
+        } else {
+          a0[j] = ub[(int64_t)jj * D];
+          a1[j] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float wj = (j0 + j < cnt) ? __shfl(w, j0 + j) : 0.f;
+        U0 += wj * a0[j];
+        U1 += wj * a1[j];
       }
     }
   }
@@ -291,12 +305,19 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
 DecodePlan decode_plan(int B, int H_q, int H_kv, int N_kv, int d) {
   const int G = H_q / H_kv;
   const int64_t units = (int64_t)B * H_kv * ((G + kQCols - 1) / kQCols);
-  // aim for about 8192 workgroups in all, chunks of at least 256 keys
-  int64_t want = (8192 + units - 1) / units;
+  // Streaming reads run fastest when the grid fills the chip once: about two
+  // resident workgroups on each of 256 compute units, so aim for 512 in all,
+  // with chunks of at least 256 keys.
+  int64_t want = (512 + units - 1) / units;
   if (want < 1) want = 1;
   int64_t chunk = ((int64_t)N_kv + want - 1) / want;
   chunk = ((chunk + kStepKeys - 1) / kStepKeys) * kStepKeys;
   if (chunk < 256) chunk = 256;
+  // tuning override (keys per split, rounded up to a multiple of 128)
+  if (const char* e = getenv("ATTN_DECODE_CHUNK")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v > 0 && v <= (1L << 24)) chunk = ((v + kStepKeys - 1) / kStepKeys) * kStepKeys;
+  }
   DecodePlan p;
   p.chunk = (int)chunk;
   p.splits = N_kv > 0 ? (int)((N_kv + chunk - 1) / chunk) : 1;

@@ -105,3 +105,11 @@ def test_decode_config5_full_size(ragged):
             assert err <= TOL_O[cfg.dtype], f"(b={b}, h={h}) max |err| {err}"
             check_lse(lg[b, h], lref, TOL_LSE[cfg.dtype])
     print(f"{cfg.name}: worst max|err| = {worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("chunk", [128, 384, 1024, 8192])
+def test_decode_split_size_does_not_change_the_result(chunk, monkeypatch):
+    """The split of the KV sequence is a performance choice only: every split size
+    matches the oracle (and so each other) within the tolerance."""
+    monkeypatch.setenv("ATTN_DECODE_CHUNK", str(chunk))
+    _decode_case(3, 16, 2, 5000, 128, "bf16", [5000, 1, 2600], seed=91)
