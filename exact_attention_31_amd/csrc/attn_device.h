@@ -67,6 +67,9 @@ struct F16 {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max of three (one v_max3_f32)
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
 // Exchange with the lane 32 positions away (the other half of the wavefront).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
@@ -82,6 +85,12 @@ __device__ __forceinline__ float half_sum(float x) {
                                                   __builtin_bit_cast(uint32_t, x), false, false);
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
+
+// Wait until every vector-memory load this wavefront issued has returned
+// (s_waitcnt vmcnt(0); other counters untouched). Placed before a loop, it keeps
+// the compiler from treating prologue loads as possibly in flight inside the
+// loop, where in-order counting would otherwise stall on fresh prefetches.
+__device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // True in every lane if `p` holds in any lane of the wavefront (uniform branch).
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }

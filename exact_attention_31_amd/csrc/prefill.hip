@@ -50,8 +50,15 @@ template <int D> struct Lds16 {
 // common reference point, so u / l is unchanged.
 constexpr float kLazyRescale = 8.f;
 
-template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(
+// QB query blocks of 32 rows per wavefront (QB = 1: 128 rows per workgroup,
+// QB = 2: 256). Each K or V operand read from LDS feeds QB MFMAs, so QB = 2
+// halves the LDS bytes per FLOP at the price of twice the registers.
+template <int QB, int D> struct Occ {
+  static constexpr int kWaves = (QB == 2 && D == 128) ? 1 : 2;  // wavefronts per SIMD
+};
+
+template <class TT, int D, bool CAUSAL, int QB>
+__global__ __launch_bounds__(kThreads, (Occ<QB, D>::kWaves)) void prefill16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
     float scale_log2, int nqb) {
@@ -61,17 +68,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(
   constexpr int DB = D / 32;   // 32-wide blocks of the output
   constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
   constexpr int LPT = kBN * CPR / kThreads;  // 16-byte loads per thread per tile, per tensor
+  constexpr int BM = 4 * 32 * QB;            // query rows per workgroup
   static_assert(LPT * kThreads == kBN * CPR, "tile load must split evenly");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * KST];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBN * VST];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // scalar, so that every per-wavefront decision below is a uniform branch
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31;
   const int lh = lane >> 5;
   // causal: longest query blocks first
-  const int qb = CAUSAL ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+  const int qblk = CAUSAL ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int hk = h / (H_q / H_kv);
@@ -82,20 +91,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(
   const auto rK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
   const auto rV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
 
-  const int q0 = qb * kBM + wave * 32;  // first row of this wavefront
-  const int qrow = q0 + lr;             // this lane's row
-  const int off = N_kv - N_q;           // bottom-right causal alignment
-  // keys below `lim` are visible to this lane's row
-  const int lim = CAUSAL ? min(N_kv, max(qrow + off + 1, 0)) : N_kv;
-
-  // Q^T operand: lane holds row qrow, d = 16*s + 8*lh + 0..7 (rows past N_q read as 0)
-  u32x4_t qreg[KS];
+  const int q0 = qblk * BM + wave * 32 * QB;  // first row of this wavefront
+  const int off = N_kv - N_q;                 // bottom-right causal alignment
+  int qrow[QB], lim[QB];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qreg[s] = buffer_load16(rQ, (uint32_t)(qrow * D + 16 * s + 8 * lh) * 2);
+  for (int j = 0; j < QB; ++j) {
+    qrow[j] = q0 + 32 * j + lr;  // this lane's row in query block j
+    // keys below lim[j] are visible to that row
+    lim[j] = CAUSAL ? min(N_kv, max(qrow[j] + off + 1, 0)) : N_kv;
+  }
+
+  // Q^T operand: lane holds row qrow[j], d = 16*s + 8*lh + 0..7 (rows past N_q read as 0)
+  u32x4_t qreg[QB][KS];
+#pragma unroll
+  for (int j = 0; j < QB; ++j)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qreg[j][s] = buffer_load16(rQ, (uint32_t)(qrow[j] * D + 16 * s + 8 * lh) * 2);
 
   int kv_end = N_kv;
   if (CAUSAL) {
-    const int qlast = min(qb * kBM + kBM - 1, N_q - 1);
+    const int qlast = min(qblk * BM + BM - 1, N_q - 1);
     kv_end = min(N_kv, qlast + off + 1);
   }
   const int ntiles = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
@@ -111,6 +127,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(
     st_k[i] = r * KST + cc * 8;
     st_v[i] = r * VST + cc * 8;
   }
+  // per-lane LDS offsets of the MFMA operands (elements):
+  //   K: row lr (+32 for the second key block), columns 16*st + 8*lh
+  //   V (transposing read): lane i of 16-lane group g reads row 4*(g/2) + i/4,
+  //   columns 16*(g%2) + 4*(i%4)
+  const int k_lane = lr * KST + 8 * lh;
+  const int v_lane = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * VST + 16 * ((lane >> 4) & 1) +
+                     4 * (lane & 3);
   u32x4_t kbuf[LPT], vbuf[LPT];
   auto load_tile = [&](int t) {
     const uint32_t base = (uint32_t)(t * kBN) * D * 2;
@@ -128,16 +151,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(
     }
   };
 
-  f32x16_t oacc[DB];
+  f32x16_t oacc[QB][DB];
+  float m[QB], l[QB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16_t{0};
-  float m = kNegInf;  // reference maximum, in units of log2 (scores * scale * log2 e)
-  float l = 0.f;      // this half-wave's part of the denominator
-
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  for (int j = 0; j < QB; ++j) {
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[j][i] = f32x16_t{0};
+    m[j] = kNegInf;  // reference maximum, in units of log2 (scores * scale * log2 e)
+    l[j] = 0.f;      // this half-wave's part of the denominator
   }
+
+  // Tile 0 is staged unconditionally (loads past the end read zeros): with no
+  // branch here every load issued so far has completed when the loop starts,
+  // so the loop only ever waits for its own prefetch, at the LDS store.
+  load_tile(0);
+  store_tile(0);
+  vmem_wait_all();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -145,74 +174,86 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(
     if (t + 1 < ntiles) load_tile(t + 1);  // in flight during this tile's math
     const int kv0 = t * kBN;
     // wavefront-uniform: does this tile hold any key visible to this wavefront?
-    const bool live = !CAUSAL || kv0 <= q0 + 31 + off;
+    const bool live = !CAUSAL || kv0 <= q0 + 32 * QB - 1 + off;
     if (live) {
-      const uint16_t* tK = sK[buf];
-      const uint16_t* tV = sV[buf];
-      // ---- S^T = K Q^T for two 32-key blocks
-      f32x16_t s0 = f32x16_t{0}, s1 = f32x16_t{0};
+      const uint16_t* tK = &sK[0][0] + buf * (kBN * KST) + k_lane;
+      const uint16_t* tV = &sV[0][0] + buf * (kBN * VST) + v_lane;
+      // ---- S^T = K Q^T: two 32-key blocks x QB query blocks; each K read feeds QB MFMAs
+      f32x16_t s[QB][2];
+#pragma unroll
+      for (int j = 0; j < QB; ++j) s[j][0] = s[j][1] = f32x16_t{0};
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        const u32x4_t a0 = *(const u32x4_t*)(tK + lr * KST + 16 * st + 8 * lh);
-        const u32x4_t a1 = *(const u32x4_t*)(tK + (32 + lr) * KST + 16 * st + 8 * lh);
-        s0 = TT::mfma32(a0, qreg[st], s0);
-        s1 = TT::mfma32(a1, qreg[st], s1);
+        const u32x4_t a0 = *(const u32x4_t*)(tK + 16 * st);
+        const u32x4_t a1 = *(const u32x4_t*)(tK + 32 * KST + 16 * st);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+          s[j][0] = TT::mfma32(a0, qreg[j][st], s[j][0]);
+          s[j][1] = TT::mfma32(a1, qreg[j][st], s[j][1]);
+        }
       }
       // ---- mask (tail and causal diagonal tiles only), branch-free per element
       const bool need_mask = (kv0 + kBN > N_kv) || (CAUSAL && kv0 + kBN - 1 > q0 + off);
       if (need_mask) {
         const int kvb = kv0 + 4 * lh;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kv = kvb + 8 * (r >> 2) + (r & 3);
-          s0[r] = (kv < lim) ? s0[r] : kNegInf;
-          s1[r] = (kv + 32 < lim) ? s1[r] : kNegInf;
+        for (int j = 0; j < QB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kv = kvb + 8 * (r >> 2) + (r & 3);
+            s[j][0][r] = (kv < lim[j]) ? s[j][0][r] : kNegInf;
+            s[j][1][r] = (kv + 32 < lim[j]) ? s[j][1][r] : kNegInf;
+          }
+      }
+      uint32_t pk[QB][16];
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        // ---- row max of the raw scores (scale > 0 commutes with max)
+        float mx = max3(s[j][0][0], s[j][0][1], s[j][1][0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = max3(mx, s[j][0][r], s[j][1][r]);
+        mx = fmaxf(mx, s[j][1][0]);
+        const float mxs = half_max(mx) * scale_log2;
+        // The branch is wavefront-uniform, but each lane moves only its own
+        // reference (alpha = 1 is an exact multiply), so a row's arithmetic never
+        // depends on the other rows of the wavefront.
+        const bool need = mxs > m[j] + kLazyRescale;
+        if (wave_any(need)) {
+          const float alpha = need ? ((m[j] == kNegInf) ? 0.f : fast_exp2(m[j] - mxs)) : 1.f;
+          m[j] = need ? mxs : m[j];
+          l[j] *= alpha;
+#pragma unroll
+          for (int i = 0; i < DB; ++i) oacc[j][i] *= alpha;
+        }
+        const float nm = (m[j] == kNegInf) ? 0.f : -m[j];
+        // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[j][0][r], scale_log2, nm));
+          const float p1 = fast_exp2(__builtin_fmaf(s[j][0][r + 1], scale_log2, nm));
+          const float p2 = fast_exp2(__builtin_fmaf(s[j][1][r], scale_log2, nm));
+          const float p3 = fast_exp2(__builtin_fmaf(s[j][1][r + 1], scale_log2, nm));
+          l[j] += (p0 + p1) + (p2 + p3);
+          pk[j][r >> 1] = TT::pack2(p0, p1);
+          pk[j][8 + (r >> 1)] = TT::pack2(p2, p3);
         }
       }
-      // ---- row max of the raw scores (scale > 0 commutes with max)
-      float mx = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      const float mxs = half_max(mx) * scale_log2;
-      // The branch is wavefront-uniform, but each lane moves only its own
-      // reference (alpha = 1 is an exact multiply), so a row's arithmetic never
-      // depends on the other rows of the wavefront.
-      const bool need = mxs > m + kLazyRescale;
-      if (wave_any(need)) {
-        const float alpha = need ? ((m == kNegInf) ? 0.f : fast_exp2(m - mxs)) : 1.f;
-        m = need ? mxs : m;
-        l *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-      }
-      const float nm = (m == kNegInf) ? 0.f : -m;
-      // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
-      uint32_t pk[16];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s0[r], scale_log2, nm));
-        const float p1 = fast_exp2(__builtin_fmaf(s0[r + 1], scale_log2, nm));
-        const float p2 = fast_exp2(__builtin_fmaf(s1[r], scale_log2, nm));
-        const float p3 = fast_exp2(__builtin_fmaf(s1[r + 1], scale_log2, nm));
-        l += (p0 + p1) + (p2 + p3);
-        pk[r >> 1] = TT::pack2(p0, p1);
-        pk[8 + (r >> 1)] = TT::pack2(p2, p3);
-      }
-      // ---- O^T += V^T P^T, four 16-key steps; V^T through the transposing LDS read
-      const int g = lane >> 4;   // 16-lane group
-      const int gi = lane & 15;  // lane within group
+      // ---- O^T += V^T P^T, four 16-key steps; V^T through the transposing LDS read,
+      // each V operand feeding QB MFMAs
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        const u32x4_t bop = {pk[4 * t4 + 0], pk[4 * t4 + 1], pk[4 * t4 + 2], pk[4 * t4 + 3]};
-        // key rows of this lane's K-slots: 16*t4 + 4*lh + {0..3}, then the same + 8
-        const int krow = 16 * t4 + 4 * (g >> 1) + (gi >> 2);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int dcol = db * 32 + 16 * (g & 1) + 4 * (gi & 3);
-          const u32x2_t lo = lds_read_tr16(tV + krow * VST + dcol);
-          const u32x2_t hi = lds_read_tr16(tV + (krow + 8) * VST + dcol);
+          // key rows 16*t4 + 4*lh + {0..3} (then + 8), columns db*32 + this lane's 16-group
+          const u32x2_t lo = lds_read_tr16(tV + 16 * t4 * VST + db * 32);
+          const u32x2_t hi = lds_read_tr16(tV + (16 * t4 + 8) * VST + db * 32);
           const u32x4_t aop = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = TT::mfma32(aop, bop, oacc[db]);
+#pragma unroll
+          for (int j = 0; j < QB; ++j) {
+            const u32x4_t bop = {pk[j][4 * t4 + 0], pk[j][4 * t4 + 1], pk[j][4 * t4 + 2],
+                                 pk[j][4 * t4 + 3]};
+            oacc[j][db] = TT::mfma32(aop, bop, oacc[j][db]);
+          }
         }
       }
     }
@@ -221,21 +262,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(
   }
 
   // ---- epilogue: combine half-wave denominators, normalise, store (rows past N_q dropped)
-  l = half_sum(l);
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
   const auto rO = buffer_rsrc(O + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+  for (int j = 0; j < QB; ++j) {
+    const float lt = half_sum(l[j]);
+    const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d = db * 32 + 8 * rg + 4 * lh;
-      const u32x2_t w = {TT::pack2(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv),
-                         TT::pack2(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv)};
-      buffer_store8(rO, (uint32_t)(qrow * D + d) * 2, w);
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = db * 32 + 8 * rg + 4 * lh;
+        const u32x2_t w = {TT::pack2(oacc[j][db][4 * rg + 0] * inv, oacc[j][db][4 * rg + 1] * inv),
+                           TT::pack2(oacc[j][db][4 * rg + 2] * inv, oacc[j][db][4 * rg + 3] * inv)};
+        buffer_store8(rO, (uint32_t)(qrow[j] * D + d) * 2, w);
+      }
     }
-  }
-  if (LSE != nullptr && lh == 0 && qrow < N_q) {
-    LSE[((int64_t)b * H_q + h) * N_q + qrow] = (l > 0.f) ? (m + log2f(l)) * kLn2 : kNegInf;
+    if (LSE != nullptr && lh == 0 && qrow[j] < N_q) {
+      LSE[((int64_t)b * H_q + h) * N_q + qrow[j]] = (lt > 0.f) ? (m[j] + log2f(lt)) * kLn2 : kNegInf;
+    }
   }
 }
 
@@ -354,9 +398,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill32_kernel(
   }
 }
 
-template <class TT, int D>
-hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
-  const int nqb = (a.N_q + kBM - 1) / kBM;
+template <class TT, int D, int QB>
+hipError_t launch16q(const PrefillArgs& a, hipStream_t st) {
+  constexpr int BM = 4 * 32 * QB;
+  const int nqb = (a.N_q + BM - 1) / BM;
   dim3 grid(nqb, a.H_q, a.B);
   const float sl2 = a.scale * kLog2e;
   auto q = (const uint16_t*)a.q;
@@ -364,12 +409,17 @@ hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
   auto v = (const uint16_t*)a.v;
   auto o = (uint16_t*)a.o;
   if (a.causal)
-    hipLaunchKernelGGL((prefill16_kernel<TT, D, true>), grid, dim3(kThreads), 0, st, q, k, v, o,
-                       a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb);
+    hipLaunchKernelGGL((prefill16_kernel<TT, D, true, QB>), grid, dim3(kThreads), 0, st, q, k, v,
+                       o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb);
   else
-    hipLaunchKernelGGL((prefill16_kernel<TT, D, false>), grid, dim3(kThreads), 0, st, q, k, v, o,
-                       a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb);
+    hipLaunchKernelGGL((prefill16_kernel<TT, D, false, QB>), grid, dim3(kThreads), 0, st, q, k, v,
+                       o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb);
   return hipGetLastError();
+}
+
+template <class TT, int D>
+hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
+  return launch16q<TT, D, 1>(a, st);
 }
 
 template <int D>
