@@ -87,7 +87,12 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
   int st = check_common(B, H_q, H_kv, N_q, N_kv, d, dtype, scale);
   if (st != ATTN_OK) return st;
   if (causal != 0 && causal != 1) return ATTN_ERR_VALUE;
-  if ((int64_t)(N_q + 127) / 128 > 0x7fffffff) return ATTN_ERR_SHAPE;
+  // one workgroup per (batch, head, 128-row query block) on a 1-D grid
+  if ((int64_t)((N_q + 127) / 128) * H_q * B > 0x7ffffff0LL) return ATTN_ERR_SHAPE;
+  // per-head byte offsets are 32-bit (buffer addressing)
+  if ((int64_t)N_q * d * elem_size(dtype) > 0xffffffffLL ||
+      (int64_t)N_kv * d * elem_size(dtype) > 0xffffffffLL)
+    return ATTN_ERR_SHAPE;
   if (B == 0 || H_q == 0 || N_q == 0) return ATTN_OK;
   if (q == nullptr || o == nullptr) return ATTN_ERR_NULL;
   if (N_kv > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
