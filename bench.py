@@ -146,6 +146,40 @@ def bench_decode(cfg, steps, warmup, torch, E, ragged=False):
             "wall_s": wall}
 
 
+def copy_calibration(torch, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size (torch's copy kernel): the
+    HBM counters read for it calibrate the FETCH_SIZE / WRITE_SIZE scale."""
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    return {"copy_bytes": nbytes, "reps": reps}
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash(name: str) -> str:
+    import hashlib
+    path = os.path.join(ROOT, "exact_attention_31_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch from the committed counter runs, or None when the
+    kernel source changed after they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != kernel_source_hash(rec["source"]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def cpu_baseline(cfg, budget_s=15.0):
     """The float64 oracle on a bounded sample of the prefill workload (whole heads)."""
     import attn_inputs as A
@@ -185,6 +219,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["prefill", "decode", "decode_ragged"], default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
@@ -199,6 +235,9 @@ def main(argv=None):
         print("no GPU visible", file=sys.stderr)
         return 3
     props = torch.cuda.get_device_properties(0)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(torch)), flush=True)
+        return 0
 
     res = {}
     if args.only in (None, "prefill"):
@@ -247,7 +286,8 @@ def main(argv=None):
     if p:
         line["roofline"] = {"bound": "mfma", "achieved": round(p["tflops"], 3), "peak": PEAK_MFMA_16BIT,
                             "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_MFMA_16BIT, 4),
-                            "traffic": None, "kernel": "prefill16_kernel<BF16,128,causal>",
+                            "traffic": measured_traffic("prefill"),
+                            "kernel": "prefill16_kernel<BF16,128,causal>",
                             "work_per_launch": p["flops"]}
     if d:
         line["decode"] = {"workload": "GQA decode, bf16, B=64, H_q=32, H_kv=4 (G=8), d=128, "
@@ -255,7 +295,8 @@ def main(argv=None):
                           "value": round(d["gb_per_s"], 2), "unit": "GB/s",
                           "frac_of_hbm_peak": round(d["frac_of_peak"], 4)}
         line["decode_roofline"] = {"bound": "hbm", "achieved": round(d["gb_per_s"], 2), "peak": PEAK_HBM,
-                                   "unit": "GB/s", "frac": round(d["frac_of_peak"], 4), "traffic": None,
+                                   "unit": "GB/s", "frac": round(d["frac_of_peak"], 4),
+                                   "traffic": measured_traffic("decode"),
                                    "kernel": "decode_split_kernel + decode_merge_kernel (one step)",
                                    "work_per_launch": d["kv_bytes"]}
     if p:
