@@ -87,8 +87,8 @@ template <int QB, int D> struct Occ {
   static constexpr int kWaves = (QB == 2 && D == 128) ? 1 : 2;  // wavefronts per SIMD
 };
 
-template <class TT, int D, bool CAUSAL, int QB>
-__global__ __launch_bounds__(kThreads, (Occ<QB, D>::kWaves)) void prefill16_kernel(
+template <class TT, int D, bool CAUSAL, int QB, int NW = 4>
+__global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void prefill16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
     float scale_log2, int nqb, int nbatch) {
@@ -97,9 +97,10 @@ __global__ __launch_bounds__(kThreads, (Occ<QB, D>::kWaves)) void prefill16_kern
   constexpr int KS = D / 16;   // k-steps of the score MFMA
   constexpr int DB = D / 32;   // 32-wide blocks of the output
   constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
-  constexpr int LPT = kBN * CPR / kThreads;  // 16-byte loads per thread per tile, per tensor
-  constexpr int BM = 4 * 32 * QB;            // query rows per workgroup
-  static_assert(LPT * kThreads == kBN * CPR, "tile load must split evenly");
+  constexpr int NT = 64 * NW;                // threads per workgroup
+  constexpr int LPT = kBN * CPR / NT;        // 16-byte loads per thread per tile, per tensor
+  constexpr int BM = NW * 32 * QB;           // query rows per workgroup
+  static_assert(LPT * NT == kBN * CPR, "tile load must split evenly");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * KST];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBN * VST];
 
@@ -146,12 +147,12 @@ __global__ __launch_bounds__(kThreads, (Occ<QB, D>::kWaves)) void prefill16_kern
   }
   const int ntiles = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
 
-  // this thread's share of each tile: chunk c = tid + kThreads*i -> row c / CPR, column c % CPR
+  // this thread's share of each tile: chunk c = tid + NT*i -> row c / CPR, column c % CPR
   uint32_t ld_off[LPT];
   int st_k[LPT], st_v[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
-    const int c = tid + kThreads * i;
+    const int c = tid + NT * i;
     const int r = c / CPR, cc = c % CPR;
     ld_off[i] = (uint32_t)(r * D + cc * 8) * 2;
     st_k[i] = r * KST + cc * 8;
@@ -1339,9 +1340,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill32_kernel(
 // 1-D grid covering `items` work items, rounded up to a multiple of the 8 XCDs.
 inline int xcd_grid(int64_t items) { return (int)(((items + 7) / 8) * 8); }
 
-template <class TT, int D, int QB>
+template <class TT, int D, int QB, int NW = 4>
 hipError_t launch16q(const PrefillArgs& a, hipStream_t st) {
-  constexpr int BM = 4 * 32 * QB;
+  constexpr int BM = NW * 32 * QB;
   const int nqb = (a.N_q + BM - 1) / BM;
   dim3 grid(xcd_grid((int64_t)nqb * a.H_q * a.B));
   const float sl2 = a.scale * kLog2e;
@@ -1350,10 +1351,10 @@ hipError_t launch16q(const PrefillArgs& a, hipStream_t st) {
   auto v = (const uint16_t*)a.v;
   auto o = (uint16_t*)a.o;
   if (a.causal)
-    hipLaunchKernelGGL((prefill16_kernel<TT, D, true, QB>), grid, dim3(kThreads), 0, st, q, k, v,
+    hipLaunchKernelGGL((prefill16_kernel<TT, D, true, QB, NW>), grid, dim3(64 * NW), 0, st, q, k, v,
                        o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
   else
-    hipLaunchKernelGGL((prefill16_kernel<TT, D, false, QB>), grid, dim3(kThreads), 0, st, q, k, v,
+    hipLaunchKernelGGL((prefill16_kernel<TT, D, false, QB, NW>), grid, dim3(64 * NW), 0, st, q, k, v,
                        o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
   return hipGetLastError();
 }
@@ -1430,9 +1431,13 @@ hipError_t launch16w2(const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Kernel form for 16-bit inputs: the loop with one query block per wavefront
-// by default; ATTN_PREFILL_VARIANT=2 selects two query blocks per wavefront and
-// 3 the software-pipelined loop (tuning overrides).
+// Kernel form for 16-bit inputs: one 32-row query block per wavefront, 8
+// wavefronts (256 rows) per workgroup for d = 128 and 4 (128 rows) for d = 64,
+// where the smaller register footprint buys a third resident wavefront per
+// SIMD instead. ATTN_PREFILL_VARIANT selects alternative forms (tuning only):
+// 1 = 4 wavefronts, 2 = two query blocks per wavefront, 3 = software-pipelined
+// scores, 4 = two ping-ponging wavefront groups, 5 = direct-load 3-stage ring,
+// 6 = two query blocks with a direct-load ring, 7 = 8 wavefronts.
 template <class TT, int D>
 hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
   static const int variant = [] {
@@ -1443,8 +1448,10 @@ hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
   if (variant == 3) return launch16p<TT, D>(a, st);
   if (variant == 4) return launch16pp<TT, D>(a, st);
   if (variant == 5) return launch16dl<TT, D>(a, st);
+  if (variant == 1) return launch16q<TT, D, 1, 4>(a, st);
   if (variant == 6) return launch16w2<TT, D>(a, st);
-  return launch16q<TT, D, 1>(a, st);
+  if (variant == 7) return launch16q<TT, D, 1, 8>(a, st);
+  return launch16q<TT, D, 1, (D == 128 ? 8 : 4)>(a, st);
 }
 
 template <int D>
