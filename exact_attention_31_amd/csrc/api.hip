@@ -12,6 +12,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 int g_dev_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+int g_dev_cus[kMaxDevices];
 std::mutex g_dev_mu;
 
 // ATTN_OK if the current device is a gfx950; cached per device.
@@ -35,6 +36,7 @@ int check_device() {
       return ATTN_ERR_NO_DEVICE;
     }
     g_dev_ok[dev] = (strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_dev_cus[dev] = p.multiProcessorCount;
   }
   return g_dev_ok[dev] == 1 ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
 }
@@ -147,8 +149,10 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, con
   st = check_device();
   if (st != ATTN_OK) return st;
   float* ws = (float*)workspace;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
   attn::DecodeArgs a{q, k_cache, v_cache, kv_lens, o, lse, B, H_q, H_kv, N_kv, d, scale, dtype,
-                     plan.chunk, plan.splits, ws,
+                     plan.chunk, plan.splits, g_dev_cus[dev], ws,
                      ws + (size_t)B * H_q * plan.splits * d};
   return attn::launch_decode(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

@@ -35,6 +35,7 @@ struct DecodeArgs {
   int dtype;
   int chunk;   // keys per split
   int splits;  // splits per (request, KV head), = ceil(N_kv / chunk)
+  int num_cus; // compute units of the device (sizes the persistent grid)
   float* part_u;   // [B, H_q, splits, d] un-normalised partial outputs
   float* part_ml;  // [B, H_q, splits, 2] partial (max in log2 units, denominator)
 };

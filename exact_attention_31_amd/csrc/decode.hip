@@ -11,8 +11,9 @@
 // rescaling that the online softmax applies between blocks (auturnal.com
 // transformer-attention guide, section 8), applied across partitions.
 //
-// gfx950 mapping: a workgroup (4 wavefronts) takes one (request, KV head,
-// chunk); each wavefront takes 32 keys per step. K rows go straight from HBM
+// gfx950 mapping: a persistent grid of wavefronts takes (request, KV head,
+// chunk) units round-robin; a wavefront streams its chunk 32 keys per step with
+// the next step's loads in flight. K rows go straight from HBM
 // into the A operand of S^T = K Q^T (v_mfma_f32_16x16x32, 16-byte loads); the
 // group's query heads form the B operand (padded to 16 columns). V rows are
 // staged in LDS and read back transposed (ds_read_b64_tr_b16) as the A operand
@@ -39,40 +40,32 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+template <int D> struct DecLds {
+  static constexpr int VST = D + 16;              // row stride of staged V rows
+  static constexpr int kV = 4 * kWaveKeys * VST;  // V staging, 4 wavefronts (elements)
+};
+
+// One work unit, done by one wavefront alone: keys [split*chunk,
+// min((split+1)*chunk, len)) of request b for KV head hk and query-head group
+// qg. Writes that chunk's partial (u, m, l) for the group's query heads.
 template <class TT, int D>
-__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
+__device__ __forceinline__ void wave_unit(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const int* __restrict__ kv_lens, float* __restrict__ part_u, float* __restrict__ part_ml,
-    int H_q, int H_kv, int N_kv, int splits, int chunk, float scale_log2) {
-  constexpr int VST = D + 16;       // LDS row stride of the staged V rows
+    float* __restrict__ part_u, float* __restrict__ part_ml, int H_q, int H_kv, int N_kv,
+    int splits, int chunk, float scale_log2, int b, int hk, int qg, int split, int len,
+    uint16_t* sV) {
+  constexpr int VST = DecLds<D>::VST;
   constexpr int KS = D / 32;        // k-steps of the score MFMA
   constexpr int DB = D / 16;        // 16-wide output blocks
   constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int VL = kWaveKeys * CPR / 64;        // V loads per lane per step
-  constexpr int kV = 4 * kWaveKeys * VST;          // V staging (elements)
-  constexpr int kComb = 4 * kQCols * (2 + D + 1) * 2;  // combine area, in 16-bit units
-  constexpr int kLds = kV > kComb ? kV : kComb;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kLds];
+  constexpr int VL = kWaveKeys * CPR / 64;  // V loads per lane per step
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
   const int c16 = lane & 15;   // query column (S^T) / output head
   const int g = lane >> 4;     // 16-lane group
-  const int split = blockIdx.x;
   const int G = H_q / H_kv;
-  const int ngroups = (G + kQCols - 1) / kQCols;
-  const int hk = blockIdx.y / ngroups;
-  const int qg = blockIdx.y % ngroups;
-  const int b = blockIdx.z;
-
-  int len = kv_lens ? kv_lens[b] : N_kv;
-  len = min(max(len, 0), N_kv);
-  const int start = split * chunk;
-  if (start >= len) return;  // nothing in this split (its partial is never read)
-  const int end = min(start + chunk, len);
-  // each wavefront takes a contiguous quarter of the chunk
-  const int wq = chunk / 4;
-  const int wbeg = min(start + wave * wq, end);
-  const int wend = min(wbeg + wq, end);
+  const int wbeg = split * chunk;
+  const int wend = min(wbeg + chunk, len);
   const int nsteps = (wend - wbeg + kWaveKeys - 1) / kWaveKeys;
 
   // rows past the request's length read as zeros
@@ -94,7 +87,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x4_t{0, 0, 0, 0};
   float m = kNegInf, l = 0.f;
-  uint16_t* sV = smem + wave * kWaveKeys * VST;
 
   // K rows feed the A operand directly: key = w0 + 16*kb + c16, d = 32*st + 8*g
   // V rows: lane takes chunk c = lane + 64*i -> row c / CPR, column c % CPR
@@ -124,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
 #pragma unroll
       for (int st = 0; st < KS; ++st) s[kb] = TT::mfma16(kk[kb][st], qreg[st], s[kb]);
     }
-    // mask keys past this wavefront's range, running max over its 32 keys
+    // mask keys past the chunk, running max over the step's 32 keys
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -167,7 +159,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     wave_lds_sync();  // reads done before the next step overwrites the rows
   };
 
-  if (nsteps > 0) issue(wbeg, ka[0], va[0]);
+  issue(wbeg, ka[0], va[0]);
   for (int i = 0; i < nsteps; i += 2) {
     const int w0 = wbeg + i * kWaveKeys;
     if (i + 1 < nsteps) issue(w0 + kWaveKeys, ka[1], va[1]);
@@ -178,43 +170,62 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     }
   }
 
-  // ---- combine the four wavefronts' partials through LDS
+  // ---- this chunk's partial: column c16 (query head hq0 + c16) of every lane group
   l += __shfl_xor(l, 16);
   l = half_sum(l);
-  __syncthreads();  // all wavefronts are done with their V rows
-  float* cm = (float*)smem;                 // [4][16] max
-  float* cl = cm + 4 * kQCols;              // [4][16] denominator
-  float* cu = cl + 4 * kQCols;              // [4][16][D + 1] output (padded rows)
-  constexpr int UST = D + 1;
-  if (g == 0) {
-    cm[wave * kQCols + c16] = m;
-    cl[wave * kQCols + c16] = l;
+  if (c16 < ncols) {
+    const int64_t row = ((int64_t)b * H_q + hq0 + c16) * splits + split;
+    float* pu = part_u + row * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *(f32x4_t*)(pu + 16 * db + 4 * g) = oacc[db];
+    if (g == 0) {
+      part_ml[row * 2 + 0] = m;
+      part_ml[row * 2 + 1] = l;
+    }
   }
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) cu[(wave * kQCols + c16) * UST + 16 * db + 4 * g + r] = oacc[db][r];
-  __syncthreads();
-  const int64_t row0 = ((int64_t)b * H_q + hq0) * splits + split;  // (b, hq0, split)
-  for (int e = tid; e < ncols * D; e += kThreads) {
-    const int c = e / D, d = e % D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w * kQCols + c]);
-    const float Mref = (M == kNegInf) ? 0.f : M;
-    float L = 0.f, U = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float wt = fast_exp2(cm[w * kQCols + c] - Mref);
-      L += wt * cl[w * kQCols + c];
-      U += wt * cu[(w * kQCols + c) * UST + d];
+}
+
+// Persistent split kernel with a static, balanced schedule. Work units are
+// (request b, KV-head group hg, chunk c of request b), numbered chunk-major over
+// the concatenated requests: unit u covers global chunk u / HG and head group
+// u % HG. Every unit holds `chunk` keys except the last chunk of a request, so
+// handing units out round-robin to the wavefronts of the grid balances ragged
+// lengths without atomics or barriers. Each wavefront walks the requests
+// forward as its unit index grows, reading kv_lens as it goes.
+template <class TT, int D>
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const int* __restrict__ kv_lens, float* __restrict__ part_u, float* __restrict__ part_ml,
+    int B, int H_q, int H_kv, int N_kv, int splits, int chunk, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[DecLds<D>::kV];
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  uint16_t* sV = smem + wave * kWaveKeys * DecLds<D>::VST;
+  const int G = H_q / H_kv;
+  const int ngroups = (G + kQCols - 1) / kQCols;
+  const int HG = H_kv * ngroups;
+  const int nw = (int)gridDim.x * 4;
+  auto len_of = [&](int b) {
+    const int n = kv_lens ? kv_lens[b] : N_kv;
+    return min(max(n, 0), N_kv);
+  };
+  int cb = 0;                 // request holding the current global chunk
+  int cstart = 0;             // its first global chunk index
+  int lb = B > 0 ? len_of(0) : 0;
+  int cnt = (lb + chunk - 1) / chunk;
+  for (int u = (int)blockIdx.x * 4 + wave;; u += nw) {
+    const int c = u / HG, hg = u - (u / HG) * HG;
+    while (cb < B && c >= cstart + cnt) {
+      cstart += cnt;
+      ++cb;
+      if (cb < B) {
+        lb = len_of(cb);
+        cnt = (lb + chunk - 1) / chunk;
+      }
     }
-    const int64_t row = row0 + (int64_t)c * splits;
-    part_u[row * D + d] = U;
-    if (d == 0) {
-      part_ml[row * 2 + 0] = M;
-      part_ml[row * 2 + 1] = L;
-    }
+    if (cb >= B) break;
+    wave_unit<TT, D>(Q, K, V, part_u, part_ml, H_q, H_kv, N_kv, splits, chunk, scale_log2, cb,
+                     hg / ngroups, hg - (hg / ngroups) * ngroups, c - cstart, lb, sV);
   }
 }
 
@@ -287,10 +298,14 @@ template <class TT, int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   const int G = a.H_q / a.H_kv;
   const int ngroups = (G + kQCols - 1) / kQCols;
-  dim3 grid(a.splits, a.H_kv * ngroups, a.B);
+  // two resident workgroups per compute unit; never more than the units there can be
+  const int64_t units = (int64_t)a.B * a.H_kv * ngroups * a.splits;
+  const int64_t slots = 2LL * (a.num_cus > 0 ? a.num_cus : 256);  // workgroups of 4 wavefronts
+  const int64_t wgs = (units + 3) / 4;
+  dim3 grid((unsigned)(wgs < slots ? wgs : slots));
   hipLaunchKernelGGL((decode_split_kernel<TT, D>), grid, dim3(kThreads), 0, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.kv_lens,
-                     a.part_u, a.part_ml, a.H_q, a.H_kv, a.N_kv, a.splits, a.chunk,
+                     a.part_u, a.part_ml, a.B, a.H_q, a.H_kv, a.N_kv, a.splits, a.chunk,
                      a.scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -305,14 +320,15 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
 DecodePlan decode_plan(int B, int H_q, int H_kv, int N_kv, int d) {
   const int G = H_q / H_kv;
   const int64_t units = (int64_t)B * H_kv * ((G + kQCols - 1) / kQCols);
-  // Streaming reads run fastest when the grid fills the chip once: about two
-  // resident workgroups on each of 256 compute units, so aim for 512 in all,
-  // with chunks of at least 256 keys.
-  int64_t want = (512 + units - 1) / units;
-  if (want < 1) want = 1;
-  int64_t chunk = ((int64_t)N_kv + want - 1) / want;
-  chunk = ((chunk + kStepKeys - 1) / kStepKeys) * kStepKeys;
-  if (chunk < 256) chunk = 256;
+  (void)units;
+  // The persistent kernel hands chunks out round-robin to wavefronts. Chunks of
+  // up to 2048 keys (1 MB of K and V at d = 128) keep ragged lengths balanced
+  // while each wavefront's start-up latency (query and first K/V loads) stays
+  // a few percent of its chunk; short caches use chunks of at least 128 keys.
+  int64_t chunk = ((int64_t)N_kv + 15) / 16;
+  chunk = ((chunk + kWaveKeys * 4 - 1) / (kWaveKeys * 4)) * (kWaveKeys * 4);
+  if (chunk < 128) chunk = 128;
+  if (chunk > 2048) chunk = 2048;
   // tuning override (keys per split, rounded up to a multiple of 128)
   if (const char* e = getenv("ATTN_DECODE_CHUNK")) {
     const long v = strtol(e, nullptr, 10);
