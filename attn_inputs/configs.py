@@ -1,9 +1,12 @@
-"""The five workload shapes of exact attention (prefill and GQA decode).
+"""The workload shapes of exact attention (prefill and GQA decode).
 
 Shapes follow the pages' workloads: a 512-step single head; causal MHA
 prefill at 4096; a one-day-at-1-second causal series (23,400 steps, 12 heads);
-causal GQA prefill at ISL 32768 with group size 8; and GQA decode against a
-32768-token KV cache for 64 requests (uniform or ragged lengths).
+causal GQA prefill at ISL 32768 with group size 8; GQA decode against a
+32768-token KV cache for 64 requests (uniform or ragged lengths); and the
+same decode with 4 new tokens per request (speculative decoding makes the
+decode product taller, which the pages name as the way decode moves toward
+compute).
 """
 from dataclasses import dataclass, field
 import math
@@ -52,6 +55,11 @@ CONFIGS = {
     5: Config(5, "GQA decode bf16 (uniform lengths)", "decode", "bf16", 64, 32, 4, 1, 32768, 128, False, 1.0),
     6: Config(5, "GQA decode bf16 (ragged lengths)", "decode", "bf16", 64, 32, 4, 1, 32768, 128, False, 1.0,
               ragged=True),
+    # multi-token decode (speculative verification of 4 draft tokens) against
+    # the same 32768-token caches as config 5: the keys and values are config
+    # 5's, the queries are 4 per request and head, causally aligned at the end
+    7: Config(5, "GQA multi-token decode bf16 (4 tokens per request)", "decode", "bf16", 64, 32, 4, 4,
+              32768, 128, True, 1.0),
 }
 
 

@@ -9,6 +9,8 @@ Default run (one JSON line on stdout):
     K and V bytes read, and reported under "decode";
   * "roofline" relates the prefill kernel's rate (from HIP events on its launch
     stream) to the bf16 MFMA peak; "decode_roofline" relates decode to HBM peak;
+  * "decode_multi_token" times the same caches with 4 new tokens per request
+    (causal, bottom-right aligned), as a speculative-decoding verifier sees it;
   * "cpu_baseline" times the float64 oracle on a bounded sample of the prefill
     workload on this host's cores.
 `--all` also times the other three workloads (fp32 single head, the 23,400-step
@@ -123,27 +125,33 @@ def bench_prefill(cfg, steps, warmup, torch, E):
             "wall_s": wall}
 
 
-def bench_decode(cfg, steps, warmup, torch, E, ragged=False):
+def bench_decode(cfg, steps, warmup, torch, E, ragged=False, cache=None):
+    """Time one decode step (split + merge kernels). `cache` = (k, v) device tensors
+    of this config's shape to reuse (configs that share caches share seeds)."""
     import attn_inputs as A
     lens = A.ragged_lengths(cfg) if ragged else np.full(cfg.B, cfg.N_kv, np.int32)
     q = make_device_tensor(cfg, "q", torch)
-    k = make_device_tensor(cfg, "k", torch)
-    v = make_device_tensor(cfg, "v", torch)
+    if cache is None:
+        cache = (make_device_tensor(cfg, "k", torch), make_device_tensor(cfg, "v", torch))
+    k, v = cache
     o = torch.empty_like(q)
     lens_d = torch.from_numpy(lens).cuda()
-    ws = torch.empty(E.attn_decode_workspace_size(cfg.B, cfg.H_q, cfg.H_kv, 1, cfg.N_kv, cfg.d, q.dtype),
+    ws = torch.empty(E.attn_decode_workspace_size(cfg.B, cfg.H_q, cfg.H_kv, cfg.N_q, cfg.N_kv, cfg.d,
+                                                  q.dtype),
                      dtype=torch.uint8, device="cuda")
 
     def call():
-        E.attn_decode_fwd(q, k, v, o, kv_lens=lens_d, scale=cfg.scale, workspace=ws)
+        E.attn_decode_fwd(q, k, v, o, kv_lens=lens_d, scale=cfg.scale, causal=cfg.causal, workspace=ws)
 
     ms, wall = time_launches(call, steps, warmup, torch)
     nbytes = decode_kv_bytes(cfg, lens)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    del q, k, v, o, ws
-    return {"config": "5r" if ragged else 5, "name": cfg.name, "ms": ms, "kv_bytes": nbytes,
+    flops = 4 * cfg.d * cfg.H_q * sum(visible_pairs(cfg.N_q, int(n), cfg.causal) for n in lens)
+    del q, o, ws
+    key = "5r" if ragged else (cfg.cid if cfg.N_q == 1 else f"{cfg.cid}x{cfg.N_q}")
+    return {"config": key, "name": cfg.name, "ms": ms, "kv_bytes": nbytes,
             "gb_per_s": gbs, "frac_of_peak": gbs / PEAK_HBM, "peak_gb_per_s": PEAK_HBM,
-            "wall_s": wall}
+            "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12, "wall_s": wall}, cache
 
 
 def copy_calibration(torch, nbytes=1 << 30, reps=3):
@@ -217,7 +225,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--all", action="store_true", help="also time configs 1, 3, 4 and ragged decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "decode_ragged"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_ragged", "decode_multi"],
+                    default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for HBM counter calibration)")
@@ -244,13 +253,21 @@ def main(argv=None):
         res["prefill"] = bench_prefill(A.CONFIGS[2], args.steps, args.warmup, torch, E)
         print(f"# prefill c2: {res['prefill']['ms']:.3f} ms  {res['prefill']['tflops']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
+    cache = None
     if args.only in (None, "decode"):
-        res["decode"] = bench_decode(A.CONFIGS[5], args.steps, args.warmup, torch, E)
+        res["decode"], cache = bench_decode(A.CONFIGS[5], args.steps, args.warmup, torch, E)
         print(f"# decode c5: {res['decode']['ms']:.3f} ms  {res['decode']['gb_per_s']:.0f} GB/s",
               file=sys.stderr, flush=True)
+    if args.only in (None, "decode_multi"):
+        r, cache = bench_decode(A.CONFIGS[7], args.steps, args.warmup, torch, E, cache=cache)
+        print(f"# decode c5, 4 tokens: {r['ms']:.3f} ms  {r['gb_per_s']:.0f} GB/s  "
+              f"{r['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        res["decode_multi"] = r
+        if args.only == "decode_multi":
+            res["decode"] = r
     extra = []
     if args.only == "decode_ragged":
-        r = bench_decode(A.CONFIGS[6], args.steps, args.warmup, torch, E, ragged=True)
+        r, cache = bench_decode(A.CONFIGS[6], args.steps, args.warmup, torch, E, ragged=True)
         print(f"# decode c5 ragged: {r['ms']:.3f} ms  {r['gb_per_s']:.0f} GB/s", file=sys.stderr, flush=True)
         res["decode"] = r
     if args.all:
@@ -259,7 +276,8 @@ def main(argv=None):
                               args.warmup, torch, E)
             extra.append(r)
             print(f"# prefill c{cid}: {r['ms']:.3f} ms  {r['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-        r = bench_decode(A.CONFIGS[6], args.steps, args.warmup, torch, E, ragged=True)
+        r, cache = bench_decode(A.CONFIGS[6], args.steps, args.warmup, torch, E, ragged=True,
+                                cache=cache)
         extra.append(r)
         print(f"# decode c5 ragged: {r['ms']:.3f} ms  {r['gb_per_s']:.0f} GB/s", file=sys.stderr, flush=True)
 
@@ -299,6 +317,14 @@ def main(argv=None):
                                    "traffic": measured_traffic("decode"),
                                    "kernel": "decode_split_kernel + decode_merge_kernel (one step)",
                                    "work_per_launch": d["kv_bytes"]}
+    dm = res.get("decode_multi")
+    if dm and dm is not d:
+        line["decode_multi_token"] = {
+            "workload": "GQA multi-token decode, bf16, B=64, 4 new tokens per request (causal, "
+                        "bottom-right), H_q=32, H_kv=4 (G=8), d=128, KV 32768 per request",
+            "ms_per_step": round(dm["ms"], 5), "value": round(dm["gb_per_s"], 2), "unit": "GB/s",
+            "frac_of_hbm_peak": round(dm["frac_of_peak"], 4), "tflops": round(dm["tflops"], 2),
+            "kernel": "decode_split_kernel + decode_merge_kernel (one step)"}
     if p:
         line["prefill_first_call_ms"] = round(p["first_call_ms"], 3)
     if cpu:

@@ -133,7 +133,8 @@ def attn_decode_workspace_size(B, H_q, H_kv, N_q, N_kv, d, dtype) -> int:
 def attn_decode_fwd(q, k_cache, v_cache, o=None, *, kv_lens=None, lse=None, causal: bool = False,
                     scale: float | None = None, workspace=None, return_lse: bool = False,
                     stream=None):
-    """Split-KV GQA decode: q [B,H_q,1,d] against caches [B,H_kv,N_kv,d] with kv_lens [B] int32."""
+    """Split-KV GQA decode: q [B,H_q,N_q,d] (1 <= N_q <= 64 new tokens per request) against
+    caches [B,H_kv,N_kv,d] whose first kv_lens[b] (int32 [B]) positions are valid."""
     lib = load()
     if q.dtype not in DTYPE_CODE:
         raise TypeError(f"unsupported dtype {q.dtype}")

@@ -57,7 +57,9 @@ int check_common(int B, int H_q, int H_kv, int N_q, int N_kv, int d, int dtype, 
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (H_kv == 0 || H_q % H_kv != 0 || (H_q == 0 && B > 0 && N_q > 0)) return ATTN_ERR_GQA;
   if (B > 65535 || H_q > 65535) return ATTN_ERR_SHAPE;
-  if (!isfinite(scale)) return ATTN_ERR_VALUE;
+  // the kernels take the running maximum of raw scores and mask with -inf, which
+  // presumes a positive scale (the attention scale is 1/sqrt(d))
+  if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_VALUE;
   return ATTN_OK;
 }
 
@@ -76,7 +78,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_NO_DEVICE: return "no HIP device available";
     case ATTN_ERR_ALIAS: return "an output overlaps an input";
-    case ATTN_ERR_VALUE: return "scale is not finite";
+    case ATTN_ERR_VALUE: return "scale is not positive and finite, or causal is not 0 or 1";
     default: return "unknown status";
   }
 }
@@ -114,8 +116,8 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
 
 size_t attn_decode_workspace_size(int B, int H_q, int H_kv, int N_q, int N_kv, int d, int dtype) {
   if (check_common(B, H_q, H_kv, N_q, N_kv, d, dtype, 1.f) != ATTN_OK) return 0;
-  if (N_q != 1) return 0;
-  return attn::decode_plan(B, H_q, H_kv, N_kv, d).workspace_bytes;
+  if (N_q < 1 || N_q > attn::kDecodeMaxNq) return 0;
+  return attn::decode_plan(B, H_q, H_kv, N_q, N_kv, d).workspace_bytes;
 }
 
 int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
@@ -126,17 +128,22 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, con
   if (st != ATTN_OK) return st;
   if (causal != 0 && causal != 1) return ATTN_ERR_VALUE;
   if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
-  if (N_q != 1) return ATTN_ERR_UNSUPPORTED;
-  if (B == 0 || H_q == 0) return ATTN_OK;
+  if (N_q > attn::kDecodeMaxNq) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || H_q == 0 || N_q == 0) return ATTN_OK;
   if (q == nullptr || o == nullptr) return ATTN_ERR_NULL;
   if (N_kv > 0 && (k_cache == nullptr || v_cache == nullptr)) return ATTN_ERR_NULL;
-  const attn::DecodePlan plan = attn::decode_plan(B, H_q, H_kv, N_kv, d);
-  if (plan.splits > 65535 || (int64_t)H_kv * ((H_q / H_kv + 15) / 16) > 65535) return ATTN_ERR_SHAPE;
+  const attn::DecodePlan plan = attn::decode_plan(B, H_q, H_kv, N_q, N_kv, d);
+  // partial rows and work units are indexed with 32-bit integers
+  const int64_t groups = ((int64_t)(H_q / H_kv) * N_q + 15) / 16;
+  if ((int64_t)B * H_q * N_q * plan.splits > 0x3fffffffLL ||
+      (int64_t)B * H_kv * groups * plan.splits > 0x3fffffffLL)
+    return ATTN_ERR_SHAPE;
+  if ((int64_t)N_kv * d * elem_size(dtype) > 0xffffffffLL) return ATTN_ERR_SHAPE;
   if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE;
   const size_t es = elem_size(dtype);
-  const size_t nq = (size_t)B * H_q * d * es;
+  const size_t nq = (size_t)B * H_q * N_q * d * es;
   const size_t nkv = (size_t)B * H_kv * N_kv * d * es;
-  const size_t nl = (size_t)B * H_q * sizeof(float);
+  const size_t nl = (size_t)B * H_q * N_q * sizeof(float);
   const size_t nw = plan.workspace_bytes;
   if (overlaps(o, nq, q, nq) || overlaps(o, nq, k_cache, nkv) || overlaps(o, nq, v_cache, nkv) ||
       overlaps(lse, nl, q, nq) || overlaps(lse, nl, k_cache, nkv) ||
@@ -151,9 +158,9 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, con
   float* ws = (float*)workspace;
   int dev = 0;
   (void)hipGetDevice(&dev);
-  attn::DecodeArgs a{q, k_cache, v_cache, kv_lens, o, lse, B, H_q, H_kv, N_kv, d, scale, dtype,
-                     plan.chunk, plan.splits, g_dev_cus[dev], ws,
-                     ws + (size_t)B * H_q * plan.splits * d};
+  attn::DecodeArgs a{q, k_cache, v_cache, kv_lens, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal,
+                     scale, dtype, plan.chunk, plan.splits, g_dev_cus[dev], ws,
+                     ws + (size_t)B * H_q * N_q * plan.splits * d};
   return attn::launch_decode(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

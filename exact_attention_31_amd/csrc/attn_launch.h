@@ -30,14 +30,15 @@ struct DecodeArgs {
   const int* kv_lens;  // device pointer or null (all N_kv)
   void* o;
   float* lse;
-  int B, H_q, H_kv, N_kv, d;
+  int B, H_q, H_kv, N_q, N_kv, d;
+  int causal;
   float scale;
   int dtype;
   int chunk;   // keys per split
   int splits;  // splits per (request, KV head), = ceil(N_kv / chunk)
   int num_cus; // compute units of the device (sizes the persistent grid)
-  float* part_u;   // [B, H_q, splits, d] un-normalised partial outputs
-  float* part_ml;  // [B, H_q, splits, 2] partial (max in log2 units, denominator)
+  float* part_u;   // [B, H_q, N_q, splits, d] un-normalised partial outputs
+  float* part_ml;  // [B, H_q, N_q, splits, 2] partial (max in log2 units, denominator)
 };
 
 // Split plan shared by the workspace query and the launch.
@@ -46,7 +47,8 @@ struct DecodePlan {
   int splits;
   size_t workspace_bytes;
 };
-DecodePlan decode_plan(int B, int H_q, int H_kv, int N_kv, int d);
+DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d);
+constexpr int kDecodeMaxNq = 64;  // query tokens per request the decode path takes
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -51,8 +51,8 @@ template <int D> struct DecLds {
 template <class TT, int D>
 __device__ __forceinline__ void wave_unit(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    float* __restrict__ part_u, float* __restrict__ part_ml, int H_q, int H_kv, int N_kv,
-    int splits, int chunk, float scale_log2, int b, int hk, int qg, int split, int len,
+    float* __restrict__ part_u, float* __restrict__ part_ml, int H_q, int H_kv, int N_q, int N_kv,
+    int causal, int splits, int chunk, float scale_log2, int b, int hk, int qg, int split, int len,
     uint16_t* sV) {
   constexpr int VST = DecLds<D>::VST;
   constexpr int KS = D / 32;        // k-steps of the score MFMA
@@ -72,13 +72,20 @@ __device__ __forceinline__ void wave_unit(
   const uint32_t valid_bytes = (uint32_t)len * D * 2;
   const auto rK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, valid_bytes);
   const auto rV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, valid_bytes);
-  const int hq0 = hk * G + qg * kQCols;       // first query head of this group
-  const int ncols = min(kQCols, G - qg * kQCols);
+  // The G query heads of KV head hk, N_q query rows each, are G*N_q contiguous
+  // rows of Q; they are the MFMA's query columns, 16 per group qg.
+  const int64_t qrow0 = ((int64_t)b * H_q + (int64_t)hk * G) * N_q;  // first row of the KV head's block
+  const int col0 = qg * kQCols;                   // first column of this group
+  const int ncols = min(kQCols, G * N_q - col0);
+  // keys below `lim` are visible to this lane's column (query row i = col % N_q,
+  // aligned so that the last query row sees the last key)
+  const int qi = (col0 + c16) % N_q;
+  const int lim = causal ? min(len, len - N_q + qi + 1) : len;
 
-  // Q^T operand: column c16 = query head hq0 + c16, K-slots d = 32*st + 8*g + 0..7
+  // Q^T operand: column c16 = row col0 + c16 of the block, K-slots d = 32*st + 8*g + 0..7
   u32x4_t qreg[KS];
   {
-    const auto rQ = buffer_rsrc(Q + ((int64_t)b * H_q + hq0) * D, (uint32_t)ncols * D * 2);
+    const auto rQ = buffer_rsrc(Q + (qrow0 + col0) * D, (uint32_t)ncols * D * 2);
 #pragma unroll
     for (int st = 0; st < KS; ++st) qreg[st] = buffer_load16(rQ, (uint32_t)(c16 * D + 32 * st + 8 * g) * 2);
   }
@@ -116,14 +123,15 @@ __device__ __forceinline__ void wave_unit(
 #pragma unroll
       for (int st = 0; st < KS; ++st) s[kb] = TT::mfma16(kk[kb][st], qreg[st], s[kb]);
     }
-    // mask keys past the chunk, running max over the step's 32 keys
+    // mask keys past the chunk or after the column's aligned diagonal; running
+    // max over the step's 32 keys
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = w0 + kb * 16 + 4 * g + r;
-        s[kb][r] = (key < wend) ? s[kb][r] : kNegInf;
+        s[kb][r] = (key < wend && key < lim) ? s[kb][r] : kNegInf;
         mx = fmaxf(mx, s[kb][r]);
       }
     }
@@ -170,11 +178,11 @@ __device__ __forceinline__ void wave_unit(
     }
   }
 
-  // ---- this chunk's partial: column c16 (query head hq0 + c16) of every lane group
+  // ---- this chunk's partial: column c16 (query row col0 + c16 of the block)
   l += __shfl_xor(l, 16);
   l = half_sum(l);
   if (c16 < ncols) {
-    const int64_t row = ((int64_t)b * H_q + hq0 + c16) * splits + split;
+    const int64_t row = (qrow0 + col0 + c16) * splits + split;
     float* pu = part_u + row * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -197,12 +205,13 @@ template <class TT, int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int* __restrict__ kv_lens, float* __restrict__ part_u, float* __restrict__ part_ml,
-    int B, int H_q, int H_kv, int N_kv, int splits, int chunk, float scale_log2) {
+    int B, int H_q, int H_kv, int N_q, int N_kv, int causal, int splits, int chunk,
+    float scale_log2) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[DecLds<D>::kV];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   uint16_t* sV = smem + wave * kWaveKeys * DecLds<D>::VST;
   const int G = H_q / H_kv;
-  const int ngroups = (G + kQCols - 1) / kQCols;
+  const int ngroups = (G * N_q + kQCols - 1) / kQCols;
   const int HG = H_kv * ngroups;
   const int nw = (int)gridDim.x * 4;
   auto len_of = [&](int b) {
@@ -224,25 +233,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
       }
     }
     if (cb >= B) break;
-    wave_unit<TT, D>(Q, K, V, part_u, part_ml, H_q, H_kv, N_kv, splits, chunk, scale_log2, cb,
-                     hg / ngroups, hg - (hg / ngroups) * ngroups, c - cstart, lb, sV);
+    wave_unit<TT, D>(Q, K, V, part_u, part_ml, H_q, H_kv, N_q, N_kv, causal, splits, chunk,
+                     scale_log2, cb, hg / ngroups, hg - (hg / ngroups) * ngroups, c - cstart, lb, sV);
   }
 }
 
 // Merge of the split partials: out = sum_s w_s u_s / sum_s w_s l_s with
-// w_s = exp2(m_s - max_s m_s). One 64-lane wavefront per (request, query head);
-// lane i owns output column i (d = 64) or columns 2i, 2i+1 (d = 128).
+// w_s = exp2(m_s - max_s m_s). One 64-lane wavefront per query row
+// (request, query head, query index); lane i owns output column i (d = 64) or
+// columns 2i, 2i+1 (d = 128).
 template <class TT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part_u, const float* __restrict__ part_ml,
-    const int* __restrict__ kv_lens, uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q,
-    int N_kv, int splits, int chunk, int BH) {
+    const int* __restrict__ kv_lens, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    int rows_per_b, int N_kv, int splits, int chunk, int BH) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int PER = D / 64;  // columns per lane
   const int lane = threadIdx.x & 63;
-  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * H_q + h)
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);  // ((b * H_q + h) * N_q + i)
   if (bh >= BH) return;
-  const int b = bh / H_q;
+  const int b = bh / rows_per_b;
   int len = kv_lens ? kv_lens[b] : N_kv;
   len = min(max(len, 0), N_kv);
   const int ns = (len + chunk - 1) / chunk;
@@ -297,7 +307,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 template <class TT, int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   const int G = a.H_q / a.H_kv;
-  const int ngroups = (G + kQCols - 1) / kQCols;
+  const int ngroups = (G * a.N_q + kQCols - 1) / kQCols;
   // two resident workgroups per compute unit; never more than the units there can be
   const int64_t units = (int64_t)a.B * a.H_kv * ngroups * a.splits;
   const int64_t slots = 2LL * (a.num_cus > 0 ? a.num_cus : 256);  // workgroups of 4 wavefronts
@@ -305,21 +315,22 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(wgs < slots ? wgs : slots));
   hipLaunchKernelGGL((decode_split_kernel<TT, D>), grid, dim3(kThreads), 0, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.kv_lens,
-                     a.part_u, a.part_ml, a.B, a.H_q, a.H_kv, a.N_kv, a.splits, a.chunk,
-                     a.scale * kLog2e);
+                     a.part_u, a.part_ml, a.B, a.H_q, a.H_kv, a.N_q, a.N_kv, a.causal, a.splits,
+                     a.chunk, a.scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int BH = a.B * a.H_q;
+  const int BH = a.B * a.H_q * a.N_q;
   hipLaunchKernelGGL((decode_merge_kernel<TT, D>), dim3((BH + 3) / 4), dim3(256), 0, st, a.part_u,
-                     a.part_ml, a.kv_lens, (uint16_t*)a.o, a.lse, a.H_q, a.N_kv, a.splits, a.chunk, BH);
+                     a.part_ml, a.kv_lens, (uint16_t*)a.o, a.lse, a.H_q * a.N_q, a.N_kv, a.splits,
+                     a.chunk, BH);
   return hipGetLastError();
 }
 
 }  // namespace
 
-DecodePlan decode_plan(int B, int H_q, int H_kv, int N_kv, int d) {
+DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d) {
   const int G = H_q / H_kv;
-  const int64_t units = (int64_t)B * H_kv * ((G + kQCols - 1) / kQCols);
+  const int64_t units = (int64_t)B * H_kv * ((G * N_q + kQCols - 1) / kQCols);
   (void)units;
   // The persistent kernel hands chunks out round-robin to wavefronts. Chunks of
   // up to 2048 keys (1 MB of K and V at d = 128) keep ragged lengths balanced
@@ -337,7 +348,7 @@ DecodePlan decode_plan(int B, int H_q, int H_kv, int N_kv, int d) {
   DecodePlan p;
   p.chunk = (int)chunk;
   p.splits = N_kv > 0 ? (int)((N_kv + chunk - 1) / chunk) : 1;
-  p.workspace_bytes = (size_t)B * H_q * p.splits * (size_t)(d + 2) * sizeof(float);
+  p.workspace_bytes = (size_t)B * H_q * N_q * p.splits * (size_t)(d + 2) * sizeof(float);
   return p;
 }
 

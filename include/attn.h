@@ -55,14 +55,15 @@ typedef enum {
   ATTN_ERR_LAUNCH = 6,      /* the HIP launch reported an error */
   ATTN_ERR_NO_DEVICE = 7,   /* no HIP device is visible */
   ATTN_ERR_ALIAS = 8,       /* an output overlaps an input */
-  ATTN_ERR_VALUE = 9        /* scale is not finite */
+  ATTN_ERR_VALUE = 9        /* scale not positive and finite, or causal not 0 or 1 */
 } attn_status_t;
 
 /*
  * Prefill (and general) forward: every query row of Q attends to the N_kv keys.
  *   q [B,H_q,N_q,d], k/v [B,H_kv,N_kv,d], o [B,H_q,N_q,d] (same dtype);
  *   lse: float32 [B,H_q,N_q] or NULL;
- *   causal: 0 or 1 (bottom-right alignment); scale: usually 1/sqrt(d).
+ *   causal: 0 or 1 (bottom-right alignment); scale: positive and finite,
+ *   usually 1/sqrt(d).
  * Empty problems (B, N_q or H_q zero) return ATTN_OK and enqueue nothing.
  * Work: 4*d FLOP per visible (query, key) pair per query head, on MFMA.
  */
@@ -72,24 +73,32 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * Bytes of device workspace attn_decode_fwd needs for these sizes (0 if the
- * sizes are invalid). The split of the KV sequence is a pure function of
- * (B, H_q, H_kv, N_kv, d), so the same sizes always need the same workspace.
+ * sizes are invalid or N_q is outside [1, 64]). The split of the KV sequence is
+ * a pure function of (B, H_q, H_kv, N_q, N_kv, d), so the same sizes always
+ * need the same workspace.
  */
 size_t attn_decode_workspace_size(int B, int H_q, int H_kv, int N_q, int N_kv, int d, int dtype);
 
 /*
- * Decode forward (split-KV, grouped-query): one query token per request against
- * a KV cache of capacity N_kv, of which the first kv_lens[b] positions are valid.
- * The KV sequence is split into chunks; each chunk produces partial (m, l, u) per
- * query head, which a second kernel merges by log-sum-exp weights exp(m_s - m)
- * (the online-softmax rescaling of the guide's section 8 applied across chunks).
- *   q [B,H_q,1,d], k_cache/v_cache [B,H_kv,N_kv,d], o [B,H_q,1,d];
+ * Decode forward (split-KV, grouped-query): N_q new query tokens per request
+ * (N_q = 1 for plain token-by-token decoding, up to 64 for multi-token decoding
+ * such as speculative verification) against a KV cache of capacity N_kv, of
+ * which the first kv_lens[b] positions are valid and already hold the new
+ * tokens' keys and values. The KV sequence is split into chunks; each chunk
+ * produces partial (m, l, u) per query row, which a second kernel merges by
+ * log-sum-exp weights exp(m_s - m) (the online-softmax rescaling of the guide's
+ * section 8 applied across chunks).
+ *   q [B,H_q,N_q,d], k_cache/v_cache [B,H_kv,N_kv,d], o [B,H_q,N_q,d];
  *   kv_lens: device int32 [B] or NULL (all N_kv); values are clamped to [0, N_kv];
- *   lse: float32 [B,H_q,1] or NULL; N_q must be 1 (else ATTN_ERR_UNSUPPORTED);
- *   causal is accepted and has no effect for a single query (it sees all keys);
+ *   lse: float32 [B,H_q,N_q] or NULL; N_q in [0, 64] (0 is a no-op; more is
+ *   ATTN_ERR_UNSUPPORTED, use attn_prefill_fwd);
+ *   causal: 0 or 1 with bottom-right alignment per request: query i of request
+ *   b sees keys j <= i + kv_lens[b] - N_q (for N_q = 1, every valid key);
+ *   scale: positive and finite;
  *   workspace: device memory of at least attn_decode_workspace_size(...) bytes,
  *   owned by the caller, overwritten by the call (no initialisation needed).
- * Work: 2 * kv_lens[b] * H_kv * d * sizeof(dtype) bytes of K and V read.
+ * Work: 2 * kv_lens[b] * H_kv * d * sizeof(dtype) bytes of K and V read, once
+ * for all N_q * H_q / H_kv query rows that share a KV head.
  */
 int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
                     void* o, float* lse, int B, int H_q, int H_kv, int N_q, int N_kv, int d,

@@ -54,6 +54,8 @@ def test_prefill_argument_errors():
     assert pf(Hq=3, Hkv=2) == 3 and pf(Hkv=0) == 3
     assert pf(d=96) == 4 and pf(d=256) == 4 and pf(dtype=7) == 4
     assert pf(scale=float("nan")) == 9 and pf(scale=float("inf")) == 9 and pf(causal=2) == 9
+    # the kernels take maxima of raw scores: the scale must be positive
+    assert pf(scale=0.0) == 9 and pf(scale=-0.125) == 9
     assert pf(o=FAKE[0]) == 8                       # output aliases q
     assert pf(lse=ctypes.cast(FAKE[3], ctypes.c_void_p)) == 8
     # empty problems are accepted without touching a device
@@ -84,15 +86,20 @@ def df(ws=P(0x7000000000), wsb=None, Nq=1, dtype=E.ATTN_BF16, lens=None, **kw):
 
 def test_decode_workspace_size():
     assert ws_size() > 0
-    assert ws_size(Nq=2) == 0 and ws_size(d=80) == 0 and ws_size(Hq=7, Hkv=2) == 0
-    # partials: (d + 2) floats per (request, query head, split)
+    assert ws_size(Nq=65) == 0 and ws_size(Nq=0) == 0
+    assert ws_size(d=80) == 0 and ws_size(Hq=7, Hkv=2) == 0
+    # partials: (d + 2) floats per (request, query head, query row, split)
     s = ws_size()
     assert s % ((128 + 2) * 4 * 2 * 8) == 0
+    assert ws_size(Nq=5) == 5 * s and ws_size(Nq=64) == 64 * s
     assert ws_size(B=64, Hq=32, Hkv=4, Nkv=32768) >= 64 * 32 * 130 * 4
 
 
 def test_decode_argument_errors():
-    assert df(Nq=2) == 4 and df(dtype=E.ATTN_F32) == 4 and df(d=32) == 4
+    assert df(Nq=65) == 4 and df(dtype=E.ATTN_F32) == 4 and df(d=32) == 4
+    assert df(Nq=0, wsb=0) == 0      # nothing to do
+    assert df(Nq=64) in (7,) and df(Nq=7) in (7,)
+    assert df(Nq=4, wsb=ws_size(Nq=3)) == 5
     assert df(ws=None) == 5 and df(wsb=16) == 5
     assert df(Hq=12, Hkv=8) == 3
     assert df(ws=FAKE[1]) == 8       # workspace overlaps the K cache

@@ -22,9 +22,10 @@ def _announce(msg):
     sys.stdout.flush()
 
 
-def _decode_case(B, Hq, Hkv, Nkv, d, dtype, lens, seed, poison=False):
-    _announce(f"decode B={B} Hq={Hq} Hkv={Hkv} Nkv={Nkv} d={d} {dtype} lens={None if lens is None else list(lens)[:6]}")
-    q = A.random_tensor((B, Hq, 1, d), seed * 3, dtype)
+def _decode_case(B, Hq, Hkv, Nkv, d, dtype, lens, seed, poison=False, Nq=1, causal=False):
+    _announce(f"decode B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} d={d} {dtype} causal={causal} "
+              f"lens={None if lens is None else list(lens)[:6]}")
+    q = A.random_tensor((B, Hq, Nq, d), seed * 3, dtype)
     k = A.random_tensor((B, Hkv, Nkv, d), seed * 3 + 1, dtype)
     v = A.random_tensor((B, Hkv, Nkv, d), seed * 3 + 2, dtype)
     kd, vd = to_device(k, dtype), to_device(v, dtype)
@@ -38,9 +39,9 @@ def _decode_case(B, Hq, Hkv, Nkv, d, dtype, lens, seed, poison=False):
                 vd[b, :, n:] = float("nan")
     scale = float(np.float32(1 / math.sqrt(d)))
     o, lse = E.attn_decode_fwd(to_device(q, dtype), kd, vd, kv_lens=lens_d, scale=scale,
-                               return_lse=True)
+                               causal=causal, return_lse=True)
     torch.cuda.synchronize()
-    oref, lref = attention_ref(q, k, v, False, scale, kv_lens=lens)
+    oref, lref = attention_ref(q, k, v, causal, scale, kv_lens=lens)
     got = to_host64(o)
     assert np.all(np.isfinite(got))
     err = max_abs_err(got, oref)
@@ -66,6 +67,50 @@ def test_decode_small_matches_oracle(case, dtype):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_decode_never_reads_past_kv_lens(dtype):
     _decode_case(3, 16, 2, 3000, 128, dtype, [2999, 5, 1500], seed=77, poison=True)
+
+
+# multi-token decode: N_q new tokens per request (speculative verification,
+# chunked prefill against a cache), bottom-right causal alignment per request
+MULTI = [
+    # B, Hq, Hkv, Nkv, d, Nq, lens
+    (2, 8, 1, 1000, 128, 4, [1000, 3]),          # request 1: fewer keys than queries
+    (3, 32, 4, 3000, 128, 7, [3000, 1500, 7]),
+    (2, 4, 4, 500, 64, 16, None),                # G * N_q = 16: one full column group
+    (1, 16, 2, 2500, 128, 33, None),             # 264 columns: ragged last group
+    (2, 8, 1, 4100, 128, 64, [4100, 2049]),      # 512 columns per KV head
+    (2, 2, 1, 5000, 64, 2, [4999, 130]),
+    (1, 8, 8, 64, 128, 64, None),                # N_q == N_kv: plain causal prefill
+]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", MULTI, ids=lambda c: "x".join(map(str, c[:6])))
+def test_decode_multi_token_matches_oracle(case, dtype, causal):
+    B, Hq, Hkv, Nkv, d, Nq, lens = case
+    _decode_case(B, Hq, Hkv, Nkv, d, dtype, lens,
+                 seed=zlib.crc32(repr((case, dtype, causal)).encode()) % 10000, Nq=Nq,
+                 causal=causal)
+
+
+@pytest.mark.parametrize("Nq", [3, 16])
+def test_decode_multi_token_never_reads_past_kv_lens(Nq):
+    _decode_case(3, 16, 2, 3000, 128, "bf16", [2999, 5, 1500], seed=78, poison=True, Nq=Nq,
+                 causal=True)
+
+
+def test_decode_multi_token_agrees_with_prefill():
+    """N_q new tokens against a full cache: the decode path and the prefill path
+    compute the same causal attention (each against the oracle's tolerance)."""
+    _announce("decode vs prefill, B=2 Hq=16 Hkv=2 Nq=8 Nkv=3000")
+    q = to_device(A.random_tensor((2, 16, 8, 128), 11, "bf16"), "bf16")
+    k = to_device(A.random_tensor((2, 2, 3000, 128), 12, "bf16"), "bf16")
+    v = to_device(A.random_tensor((2, 2, 3000, 128), 13, "bf16"), "bf16")
+    od, ld = E.attn_decode_fwd(q, k, v, causal=True, return_lse=True)
+    op, lp = E.attn_prefill_fwd(q, k, v, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert max_abs_err(to_host64(od), to_host64(op)) <= 2 * TOL_O["bf16"]
+    assert float((ld - lp).abs().max()) <= 2 * TOL_LSE["bf16"]
 
 
 def test_decode_causal_flag_is_a_no_op_for_one_query():
@@ -113,3 +158,4 @@ def test_decode_split_size_does_not_change_the_result(chunk, monkeypatch):
     matches the oracle (and so each other) within the tolerance."""
     monkeypatch.setenv("ATTN_DECODE_CHUNK", str(chunk))
     _decode_case(3, 16, 2, 5000, 128, "bf16", [5000, 1, 2600], seed=91)
+    _decode_case(2, 8, 2, 3000, 128, "bf16", [3000, 2000], seed=92, Nq=5, causal=True)

@@ -41,3 +41,5 @@ def test_config_table():
     lens = A.ragged_lengths(c[6])
     assert lens.shape == (64,) and lens.min() >= 1 and lens.max() <= 32768
     np.testing.assert_array_equal(lens, A.ragged_lengths(c[6]))
+    # multi-token decode shares config 5's caches (same seeds), 4 queries per head
+    assert (c[7].cid, c[7].N_q, c[7].N_kv, c[7].causal, c[7].G) == (5, 4, 32768, True, 8)
