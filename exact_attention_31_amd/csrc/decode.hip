@@ -30,7 +30,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaveKeys = 32;            // keys per wavefront step
 constexpr int kStepKeys = 4 * kWaveKeys; // keys per workgroup step
-constexpr int kQCols = 16;               // query heads per workgroup (MFMA N)
+constexpr int kQCols = 16;               // query rows per column group (MFMA N)
+constexpr float kLazyRescale = 8.f;      // rescale threshold, log2 units
 
 // Orders this wavefront's LDS writes before its later LDS reads (the lanes of a
 // wavefront exchange V rows through LDS; no other wavefront touches them).
@@ -46,9 +47,11 @@ template <int D> struct DecLds {
 };
 
 // One work unit, done by one wavefront alone: keys [split*chunk,
-// min((split+1)*chunk, len)) of request b for KV head hk and query-head group
-// qg. Writes that chunk's partial (u, m, l) for the group's query heads.
-template <class TT, int D>
+// min((split+1)*chunk, len)) of request b for KV head hk and query column
+// groups NG*qg .. NG*qg + NG-1 (16 columns each). Writes that chunk's partial
+// (u, m, l) for the groups' query rows. The NG groups share every K register
+// and every V operand read from LDS; only the matrix products are per group.
+template <class TT, int D, int NG>
 __device__ __forceinline__ void wave_unit(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     float* __restrict__ part_u, float* __restrict__ part_ml, int H_q, int H_kv, int N_q, int N_kv,
@@ -68,47 +71,66 @@ __device__ __forceinline__ void wave_unit(
   const int wend = min(wbeg + chunk, len);
   const int nsteps = (wend - wbeg + kWaveKeys - 1) / kWaveKeys;
 
-  // rows past the request's length read as zeros
-  const uint32_t valid_bytes = (uint32_t)len * D * 2;
-  const auto rK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, valid_bytes);
-  const auto rV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, valid_bytes);
+  // this KV head's cache rows; rows past the request's length read as zeros
+  const uint16_t* Kh = K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
+  const uint16_t* Vh = V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
   // The G query heads of KV head hk, N_q query rows each, are G*N_q contiguous
   // rows of Q; they are the MFMA's query columns, 16 per group qg.
   const int64_t qrow0 = ((int64_t)b * H_q + (int64_t)hk * G) * N_q;  // first row of the KV head's block
-  const int col0 = qg * kQCols;                   // first column of this group
-  const int ncols = min(kQCols, G * N_q - col0);
-  // keys below `lim` are visible to this lane's column (query row i = col % N_q,
-  // aligned so that the last query row sees the last key)
-  const int qi = (col0 + c16) % N_q;
-  const int lim = causal ? min(len, len - N_q + qi + 1) : len;
-
-  // Q^T operand: column c16 = row col0 + c16 of the block, K-slots d = 32*st + 8*g + 0..7
-  u32x4_t qreg[KS];
-  {
-    const auto rQ = buffer_rsrc(Q + (qrow0 + col0) * D, (uint32_t)ncols * D * 2);
+  int col0[NG], ncols[NG], lim[NG];
 #pragma unroll
-    for (int st = 0; st < KS; ++st) qreg[st] = buffer_load16(rQ, (uint32_t)(c16 * D + 32 * st + 8 * g) * 2);
+  for (int j = 0; j < NG; ++j) {
+    col0[j] = (qg * NG + j) * kQCols;   // first column of group j
+    ncols[j] = max(0, min(kQCols, G * N_q - col0[j]));
+    // keys below lim are visible to this lane's column (query row i = col % N_q,
+    // aligned so that the last query row sees the last key)
+    const int qi = (col0[j] + c16) % N_q;
+    lim[j] = causal ? min(len, len - N_q + qi + 1) : len;
   }
 
-  f32x4_t oacc[DB];
+  // Q^T operands: column c16 of group j = row col0[j] + c16 of the block,
+  // K-slots d = 32*st + 8*g + 0..7
+  u32x4_t qreg[NG][KS];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x4_t{0, 0, 0, 0};
-  float m = kNegInf, l = 0.f;
+  for (int j = 0; j < NG; ++j) {
+    const auto rQ = buffer_rsrc(Q + (qrow0 + min(col0[j], G * N_q)) * D, (uint32_t)ncols[j] * D * 2);
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      qreg[j][st] = buffer_load16(rQ, (uint32_t)(c16 * D + 32 * st + 8 * g) * 2);
+  }
+
+  f32x4_t oacc[NG][DB];
+#pragma unroll
+  for (int j = 0; j < NG; ++j)
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[j][i] = f32x4_t{0, 0, 0, 0};
+  float m[NG], l[NG];
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    m[j] = kNegInf;
+    l[j] = 0.f;
+  }
 
   // K rows feed the A operand directly: key = w0 + 16*kb + c16, d = 32*st + 8*g
-  // V rows: lane takes chunk c = lane + 64*i -> row c / CPR, column c % CPR
+  // V rows: lane takes 16-byte chunk c = lane + 64*i of the step's rows
+  // (row c / CPR, column c % CPR). Each step's loads use a resource based at
+  // its first row (wavefront-uniform, in scalar registers) and bounded by the
+  // request's length, so the per-lane offsets stay fixed across steps.
+  const uint32_t koff0 = (uint32_t)(c16 * D + 8 * g) * 2;
+  const uint32_t koff1 = koff0 + 16 * D * 2;
+  const uint32_t voff = (uint32_t)lane * 16;
   u32x4_t ka[2][2][KS], va[2][VL];
   auto issue = [&](int w0, u32x4_t (&kk)[2][KS], u32x4_t (&vv)[VL]) {
+    const uint32_t rest = (uint32_t)(len - w0) * D * 2;  // w0 < len
+    const auto rK = buffer_rsrc(Kh + (int64_t)w0 * D, rest);
+    const auto rV = buffer_rsrc(Vh + (int64_t)w0 * D, rest);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int st = 0; st < KS; ++st)
-        kk[kb][st] = buffer_load16(rK, (uint32_t)((w0 + kb * 16 + c16) * D + 32 * st + 8 * g) * 2);
-#pragma unroll
-    for (int i = 0; i < VL; ++i) {
-      const int c = lane + 64 * i;
-      vv[i] = buffer_load16(rV, (uint32_t)((w0 + c / CPR) * D + (c % CPR) * 8) * 2);
+    for (int st = 0; st < KS; ++st) {
+      kk[0][st] = buffer_load16(rK, koff0 + 64 * st);
+      kk[1][st] = buffer_load16(rK, koff1 + 64 * st);
     }
+#pragma unroll
+    for (int i = 0; i < VL; ++i) vv[i] = buffer_load16(rV, voff + 1024 * i);
   };
   auto step = [&](int w0, const u32x4_t (&kk)[2][KS], const u32x4_t (&vv)[VL]) {
 #pragma unroll
@@ -116,45 +138,54 @@ __device__ __forceinline__ void wave_unit(
       const int c = lane + 64 * i;
       *(u32x4_t*)(sV + (c / CPR) * VST + (c % CPR) * 8) = vv[i];
     }
-    f32x4_t s[2];
+    u32x4_t bop[NG];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x4_t{0, 0, 0, 0};
+    for (int j = 0; j < NG; ++j) {
+      f32x4_t s[2];
 #pragma unroll
-      for (int st = 0; st < KS; ++st) s[kb] = TT::mfma16(kk[kb][st], qreg[st], s[kb]);
-    }
-    // mask keys past the chunk or after the column's aligned diagonal; running
-    // max over the step's 32 keys
-    float mx = kNegInf;
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x4_t{0, 0, 0, 0};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = w0 + kb * 16 + 4 * g + r;
-        s[kb][r] = (key < wend && key < lim) ? s[kb][r] : kNegInf;
-        mx = fmaxf(mx, s[kb][r]);
+        for (int st = 0; st < KS; ++st) s[kb] = TT::mfma16(kk[kb][st], qreg[j][st], s[kb]);
       }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = half_max(mx) * scale_log2;
-    const float m_new = fmaxf(m, mx);
-    const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - m_new);
-    m = m_new;
-    const float nm = (m == kNegInf) ? 0.f : -m;
-    l *= alpha;
+      // mask keys past the chunk or after the column's aligned diagonal; running
+      // max over the step's 32 keys
+      float mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-    float p[2][4];
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, nm));
-        l += p[kb][r];
+        for (int r = 0; r < 4; ++r) {
+          const int key = w0 + kb * 16 + 4 * g + r;
+          s[kb][r] = (key < wend && key < lim[j]) ? s[kb][r] : kNegInf;
+          mx = fmaxf(mx, s[kb][r]);
+        }
       }
-    // K-slots of lane group g: keys 4g+0..3 (block 0) then 16+4g+0..3 (block 1)
-    const u32x4_t bop = {TT::pack2(p[0][0], p[0][1]), TT::pack2(p[0][2], p[0][3]),
-                         TT::pack2(p[1][0], p[1][1]), TT::pack2(p[1][2], p[1][3])};
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = half_max(mx) * scale_log2;
+      // lazy rescale: a column's reference maximum moves only when the step's
+      // maximum exceeds it by more than kLazyRescale (probabilities stay below
+      // 2^kLazyRescale; l and u keep a common reference, so u / l is unchanged)
+      const bool need = mx > m[j] + kLazyRescale;
+      if (wave_any(need)) {
+        const float alpha = need ? ((m[j] == kNegInf) ? 0.f : fast_exp2(m[j] - mx)) : 1.f;
+        m[j] = need ? mx : m[j];
+        l[j] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) oacc[j][i] *= alpha;
+      }
+      const float nm = (m[j] == kNegInf) ? 0.f : -m[j];
+      float p[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, nm));
+          l[j] += p[kb][r];
+        }
+      // K-slots of lane group g: keys 4g+0..3 (block 0) then 16+4g+0..3 (block 1)
+      bop[j] = u32x4_t{TT::pack2(p[0][0], p[0][1]), TT::pack2(p[0][2], p[0][3]),
+                       TT::pack2(p[1][0], p[1][1]), TT::pack2(p[1][2], p[1][3])};
+    }
     wave_lds_sync();  // V rows of this step are in LDS
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -162,7 +193,8 @@ __device__ __forceinline__ void wave_unit(
       const u32x2_t lo = lds_read_tr16(sV + (4 * g + (c16 >> 2)) * VST + dcol);
       const u32x2_t hi = lds_read_tr16(sV + (16 + 4 * g + (c16 >> 2)) * VST + dcol);
       const u32x4_t aop = {lo[0], lo[1], hi[0], hi[1]};
-      oacc[db] = TT::mfma16(aop, bop, oacc[db]);
+#pragma unroll
+      for (int j = 0; j < NG; ++j) oacc[j][db] = TT::mfma16(aop, bop[j], oacc[j][db]);
     }
     wave_lds_sync();  // reads done before the next step overwrites the rows
   };
@@ -178,18 +210,21 @@ __device__ __forceinline__ void wave_unit(
     }
   }
 
-  // ---- this chunk's partial: column c16 (query row col0 + c16 of the block)
-  l += __shfl_xor(l, 16);
-  l = half_sum(l);
-  if (c16 < ncols) {
-    const int64_t row = (qrow0 + col0 + c16) * splits + split;
-    float* pu = part_u + row * D;
+  // ---- this chunk's partials: column c16 of group j (query row col0[j] + c16)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      *(f32x4_t*)(pu + 16 * db + 4 * g) = oacc[db];
-    if (g == 0) {
-      part_ml[row * 2 + 0] = m;
-      part_ml[row * 2 + 1] = l;
+  for (int j = 0; j < NG; ++j) {
+    float lj = l[j] + __shfl_xor(l[j], 16);
+    lj = half_sum(lj);
+    if (c16 < ncols[j]) {
+      const int64_t row = (qrow0 + col0[j] + c16) * splits + split;
+      float* pu = part_u + row * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *(f32x4_t*)(pu + 16 * db + 4 * g) = oacc[j][db];
+      if (g == 0) {
+        part_ml[row * 2 + 0] = m[j];
+        part_ml[row * 2 + 1] = lj;
+      }
     }
   }
 }
@@ -201,8 +236,8 @@ __device__ __forceinline__ void wave_unit(
 // handing units out round-robin to the wavefronts of the grid balances ragged
 // lengths without atomics or barriers. Each wavefront walks the requests
 // forward as its unit index grows, reading kv_lens as it goes.
-template <class TT, int D>
-__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
+template <class TT, int D, int NG, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int* __restrict__ kv_lens, float* __restrict__ part_u, float* __restrict__ part_ml,
     int B, int H_q, int H_kv, int N_q, int N_kv, int causal, int splits, int chunk,
@@ -211,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   uint16_t* sV = smem + wave * kWaveKeys * DecLds<D>::VST;
   const int G = H_q / H_kv;
-  const int ngroups = (G * N_q + kQCols - 1) / kQCols;
+  const int ngroups = (G * N_q + NG * kQCols - 1) / (NG * kQCols);  // units of NG column groups
   const int HG = H_kv * ngroups;
   const int nw = (int)gridDim.x * 4;
   auto len_of = [&](int b) {
@@ -233,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(
       }
     }
     if (cb >= B) break;
-    wave_unit<TT, D>(Q, K, V, part_u, part_ml, H_q, H_kv, N_q, N_kv, causal, splits, chunk,
+    wave_unit<TT, D, NG>(Q, K, V, part_u, part_ml, H_q, H_kv, N_q, N_kv, causal, splits, chunk,
                      scale_log2, cb, hg / ngroups, hg - (hg / ngroups) * ngroups, c - cstart, lb, sV);
   }
 }
@@ -304,16 +339,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   if (LSE != nullptr && lane == 0) LSE[bh] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
-template <class TT, int D>
+template <class TT, int D, int NG, int OCC>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   const int G = a.H_q / a.H_kv;
-  const int ngroups = (G * a.N_q + kQCols - 1) / kQCols;
-  // two resident workgroups per compute unit; never more than the units there can be
+  const int ngroups = (G * a.N_q + NG * kQCols - 1) / (NG * kQCols);
+  // OCC resident workgroups per compute unit; never more than the units there can be
   const int64_t units = (int64_t)a.B * a.H_kv * ngroups * a.splits;
-  const int64_t slots = 2LL * (a.num_cus > 0 ? a.num_cus : 256);  // workgroups of 4 wavefronts
+  const int64_t slots = (int64_t)OCC * (a.num_cus > 0 ? a.num_cus : 256);  // workgroups of 4 wavefronts
   const int64_t wgs = (units + 3) / 4;
   dim3 grid((unsigned)(wgs < slots ? wgs : slots));
-  hipLaunchKernelGGL((decode_split_kernel<TT, D>), grid, dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((decode_split_kernel<TT, D, NG, OCC>), grid, dim3(kThreads), 0, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.kv_lens,
                      a.part_u, a.part_ml, a.B, a.H_q, a.H_kv, a.N_q, a.N_kv, a.causal, a.splits,
                      a.chunk, a.scale * kLog2e);
@@ -352,9 +387,27 @@ DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d) {
   return p;
 }
 
+template <class TT>
+hipError_t launch_dtype(const DecodeArgs& a, hipStream_t st) {
+  // more than 16 query rows per KV head: each wavefront serves two column
+  // groups, so K and V are read once per 32 rows (ATTN_DECODE_GROUPS=1 forces one)
+  const int cols = (a.H_q / a.H_kv) * a.N_q;
+  int ng = cols <= kQCols ? 1 : (cols <= 2 * kQCols ? 2 : 4);
+  if (const char* e = getenv("ATTN_DECODE_GROUPS")) {
+    const int f = atoi(e);
+    if (f == 1 || f == 2 || f == 4) ng = f;
+  }
+  if (a.d == 64) {
+    if (ng == 1) return launch_t<TT, 64, 1, 2>(a, st);
+    return ng == 2 ? launch_t<TT, 64, 2, 2>(a, st) : launch_t<TT, 64, 4, 2>(a, st);
+  }
+  if (ng == 1) return launch_t<TT, 128, 1, 2>(a, st);
+  return ng == 2 ? launch_t<TT, 128, 2, 1>(a, st) : launch_t<TT, 128, 4, 1>(a, st);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  if (a.dtype == kDtypeBF16) return a.d == 64 ? launch_t<BF16, 64>(a, st) : launch_t<BF16, 128>(a, st);
-  return a.d == 64 ? launch_t<F16, 64>(a, st) : launch_t<F16, 128>(a, st);
+  if (a.dtype == kDtypeBF16) return launch_dtype<BF16>(a, st);
+  return launch_dtype<F16>(a, st);
 }
 
 }  // namespace attn

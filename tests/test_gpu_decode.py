@@ -80,6 +80,8 @@ MULTI = [
     (2, 8, 1, 4100, 128, 64, [4100, 2049]),      # 512 columns per KV head
     (2, 2, 1, 5000, 64, 2, [4999, 130]),
     (1, 8, 8, 64, 128, 64, None),                # N_q == N_kv: plain causal prefill
+    (2, 8, 2, 1500, 64, 5, [1500, 700]),         # d = 64, 20 columns: two groups per wavefront
+    (1, 8, 1, 900, 64, 9, None),                 # d = 64, 72 columns: four groups per wavefront
 ]
 
 
@@ -159,3 +161,12 @@ def test_decode_split_size_does_not_change_the_result(chunk, monkeypatch):
     monkeypatch.setenv("ATTN_DECODE_CHUNK", str(chunk))
     _decode_case(3, 16, 2, 5000, 128, "bf16", [5000, 1, 2600], seed=91)
     _decode_case(2, 8, 2, 3000, 128, "bf16", [3000, 2000], seed=92, Nq=5, causal=True)
+
+
+@pytest.mark.parametrize("groups", ["1", "2", "4"])
+def test_decode_column_groups_per_wavefront_agree(groups, monkeypatch):
+    """How many 16-column groups one wavefront serves is a performance choice:
+    every setting matches the oracle."""
+    monkeypatch.setenv("ATTN_DECODE_GROUPS", groups)
+    _decode_case(2, 16, 2, 2100, 128, "bf16", [2100, 999], seed=93, Nq=6, causal=True)
+    _decode_case(2, 8, 2, 1100, 64, "f16", [1100, 64], seed=94, Nq=3, causal=True)
