@@ -16,8 +16,10 @@ to bf16/fp16 on the device side are both exact):
   fp16: numpy's float16 cast, which is RNE; fp32: unchanged)
 
 tensor ids: Q=0, K=1, V=2; ragged decode lengths use SeedSequence([31, cfg, 3]).
+Paged-cache block tables are a seeded permutation of the pool's blocks,
+SeedSequence([31, 2000, seed]).
 """
 from .configs import CONFIGS, Config, get_config, ragged_lengths  # noqa: F401
 from .gen import (  # noqa: F401
-    bf16_round, fp16_round, round_to_dtype, slice_values, tensor_values, random_tensor,
+    bf16_round, fp16_round, round_to_dtype, slice_values, tensor_values, random_tensor, paged_layout,
 )

@@ -72,3 +72,25 @@ def random_tensor(shape, seed: int, dtype: str, sigma: float = 1.0) -> np.ndarra
     if sigma != 1.0:
         x *= np.float32(sigma)
     return round_to_dtype(x, dtype)
+
+
+def paged_layout(lens, block_size: int, max_blocks: int, seed: int, spare: int = 0):
+    """A block table for a paged KV cache (a random allocation, no arithmetic).
+
+    Request b needs ceil(lens[b] / block_size) logical blocks; every needed block
+    gets a distinct physical block from a seeded permutation of a pool of
+    sum(needed) + spare blocks. Entries past a request's needed blocks are -1.
+    Returns (table int32 [B, max_blocks], num_blocks).
+    """
+    lens = np.asarray(lens, dtype=np.int64)
+    need = (lens + block_size - 1) // block_size
+    if np.any(need > max_blocks):
+        raise ValueError("max_blocks too small for lens")
+    num_blocks = int(need.sum()) + int(spare)
+    perm = _rng(31, 2000, seed).permutation(num_blocks).astype(np.int32)
+    table = np.full((len(lens), max_blocks), -1, dtype=np.int32)
+    pos = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[pos:pos + n]
+        pos += n
+    return table, num_blocks

@@ -49,6 +49,11 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_workspace_size.restype = sz
     lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_decode_fwd.restype = i
+    lib.attn_decode_paged_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
+    lib.attn_decode_paged_workspace_size.restype = sz
+    lib.attn_decode_paged_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i,
+                                          vp, sz, vp]
+    lib.attn_decode_paged_fwd.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -174,5 +179,62 @@ def attn_decode_fwd(q, k_cache, v_cache, o=None, *, kv_lens=None, lse=None, caus
     return (o, lse) if (return_lse or lse is not None) else o
 
 
-__all__ = ["attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_size", "attn_status_string",
+def attn_decode_paged_workspace_size(B, H_q, H_kv, N_q, max_blocks, block_size, d, dtype) -> int:
+    code = DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load().attn_decode_paged_workspace_size(B, H_q, H_kv, N_q, max_blocks, block_size, d,
+                                                       code))
+
+
+def attn_decode_paged_fwd(q, k_pool, v_pool, block_table, o=None, *, kv_lens=None, lse=None,
+                          causal: bool = False, scale: float | None = None, workspace=None,
+                          return_lse: bool = False, stream=None):
+    """Decode over a paged KV cache: q [B,H_q,N_q,d]; pools [num_blocks,H_kv,block_size,d];
+    block_table int32 [B,max_blocks] (pool block of each logical block); kv_lens int32 [B]."""
+    lib = load()
+    if q.dtype not in DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _check_tensor("q", q, q.dtype, dev)
+    _check_tensor("k_pool", k_pool, q.dtype, dev)
+    _check_tensor("v_pool", v_pool, q.dtype, dev)
+    _check_tensor("block_table", block_table, torch.int32, dev, ndim=2)
+    B, H_q, N_q, d = q.shape
+    num_blocks, H_kv, block_size, _ = k_pool.shape
+    if tuple(k_pool.shape) != (num_blocks, H_kv, block_size, d) or v_pool.shape != k_pool.shape:
+        raise ValueError("pool shapes do not match q")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have B rows")
+    max_blocks = block_table.shape[1]
+    if kv_lens is not None:
+        _check_tensor("kv_lens", kv_lens, torch.int32, dev, ndim=1)
+        if kv_lens.shape[0] != B:
+            raise ValueError("kv_lens must have B entries")
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor("o", o, q.dtype, dev)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, dev, ndim=3)
+    need = attn_decode_paged_workspace_size(B, H_q, H_kv, N_q, max_blocks, block_size, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(dev):
+        st = lib.attn_decode_paged_fwd(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                       _ptr(kv_lens), _ptr(o), _ptr(lse), B, H_q, H_kv, N_q,
+                                       max_blocks, block_size, num_blocks, d, int(bool(causal)),
+                                       float(scale), DTYPE_CODE[q.dtype], _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(dev, stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_paged_fwd")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+__all__ = ["attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_size",
+           "attn_decode_paged_fwd", "attn_decode_paged_workspace_size", "attn_status_string",
            "attn_version", "load", "AttnError", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

@@ -117,13 +117,27 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
 size_t attn_decode_workspace_size(int B, int H_q, int H_kv, int N_q, int N_kv, int d, int dtype) {
   if (check_common(B, H_q, H_kv, N_q, N_kv, d, dtype, 1.f) != ATTN_OK) return 0;
   if (N_q < 1 || N_q > attn::kDecodeMaxNq) return 0;
-  return attn::decode_plan(B, H_q, H_kv, N_q, N_kv, d).workspace_bytes;
+  return attn::decode_plan(B, H_q, H_kv, N_q, N_kv, d, false).workspace_bytes;
 }
 
-int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
-                    void* o, float* lse, int B, int H_q, int H_kv, int N_q, int N_kv, int d,
-                    int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+namespace {
+
+bool valid_block_size(int bs) { return bs >= 16 && bs <= 4096 && (bs & (bs - 1)) == 0; }
+
+int log2_of(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+// Shared validation and launch of both decode entry points. For a paged cache
+// (table != null) k and v are pools of kv_bytes each and N_kv = max_blocks *
+// block_size; for a contiguous cache they are [B, H_kv, N_kv, d].
+int decode_launch(const void* q, const void* k, const void* v, size_t kv_bytes, const int* table,
+                  int max_blocks, int block_size, int num_blocks, const int* kv_lens, void* o,
+                  float* lse, int B, int H_q, int H_kv, int N_q, int N_kv, int d, int causal,
+                  float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool paged = table != nullptr || block_size != 0;
   int st = check_common(B, H_q, H_kv, N_q, N_kv, d, dtype, scale);
   if (st != ATTN_OK) return st;
   if (causal != 0 && causal != 1) return ATTN_ERR_VALUE;
@@ -131,37 +145,93 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, con
   if (N_q > attn::kDecodeMaxNq) return ATTN_ERR_UNSUPPORTED;
   if (B == 0 || H_q == 0 || N_q == 0) return ATTN_OK;
   if (q == nullptr || o == nullptr) return ATTN_ERR_NULL;
-  if (N_kv > 0 && (k_cache == nullptr || v_cache == nullptr)) return ATTN_ERR_NULL;
-  const attn::DecodePlan plan = attn::decode_plan(B, H_q, H_kv, N_q, N_kv, d);
+  if (paged) {
+    if (max_blocks > 0 && table == nullptr) return ATTN_ERR_NULL;
+    if (num_blocks > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  } else if (N_kv > 0 && (k == nullptr || v == nullptr)) {
+    return ATTN_ERR_NULL;
+  }
+  const attn::DecodePlan plan = attn::decode_plan(B, H_q, H_kv, N_q, N_kv, d, paged);
   // partial rows and work units are indexed with 32-bit integers
   const int64_t groups = ((int64_t)(H_q / H_kv) * N_q + 15) / 16;
   if ((int64_t)B * H_q * N_q * plan.splits > 0x3fffffffLL ||
       (int64_t)B * H_kv * groups * plan.splits > 0x3fffffffLL)
     return ATTN_ERR_SHAPE;
-  if ((int64_t)N_kv * d * elem_size(dtype) > 0xffffffffLL) return ATTN_ERR_SHAPE;
+  // contiguous caches: per-head byte offsets are 32-bit (buffer addressing)
+  if (!paged && (int64_t)N_kv * d * elem_size(dtype) > 0xffffffffLL) return ATTN_ERR_SHAPE;
   if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE;
   const size_t es = elem_size(dtype);
   const size_t nq = (size_t)B * H_q * N_q * d * es;
-  const size_t nkv = (size_t)B * H_kv * N_kv * d * es;
+  const size_t nkv = kv_bytes;
   const size_t nl = (size_t)B * H_q * N_q * sizeof(float);
   const size_t nw = plan.workspace_bytes;
-  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k_cache, nkv) || overlaps(o, nq, v_cache, nkv) ||
-      overlaps(lse, nl, q, nq) || overlaps(lse, nl, k_cache, nkv) ||
-      overlaps(lse, nl, v_cache, nkv) || overlaps(lse, nl, o, nq) ||
-      overlaps(workspace, nw, q, nq) || overlaps(workspace, nw, k_cache, nkv) ||
-      overlaps(workspace, nw, v_cache, nkv) || overlaps(workspace, nw, o, nq) ||
-      overlaps(workspace, nw, lse, nl) || overlaps(kv_lens, (size_t)B * 4, o, nq) ||
-      overlaps(kv_lens, (size_t)B * 4, workspace, nw) || overlaps(kv_lens, (size_t)B * 4, lse, nl))
+  const size_t nt = paged ? (size_t)B * max_blocks * sizeof(int) : 0;
+  const size_t nlen = (size_t)B * sizeof(int);
+  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv) ||
+      overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) || overlaps(lse, nl, v, nkv) ||
+      overlaps(lse, nl, o, nq) || overlaps(workspace, nw, q, nq) ||
+      overlaps(workspace, nw, k, nkv) || overlaps(workspace, nw, v, nkv) ||
+      overlaps(workspace, nw, o, nq) || overlaps(workspace, nw, lse, nl) ||
+      overlaps(kv_lens, nlen, o, nq) || overlaps(kv_lens, nlen, workspace, nw) ||
+      overlaps(kv_lens, nlen, lse, nl) || overlaps(table, nt, o, nq) ||
+      overlaps(table, nt, lse, nl) || overlaps(table, nt, workspace, nw))
     return ATTN_ERR_ALIAS;
   st = check_device();
   if (st != ATTN_OK) return st;
   float* ws = (float*)workspace;
   int dev = 0;
   (void)hipGetDevice(&dev);
-  attn::DecodeArgs a{q, k_cache, v_cache, kv_lens, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal,
-                     scale, dtype, plan.chunk, plan.splits, g_dev_cus[dev], ws,
-                     ws + (size_t)B * H_q * N_q * plan.splits * d};
+  attn::DecodeArgs a{q, k, v, kv_lens, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale, dtype,
+                     plan.chunk, plan.splits, g_dev_cus[dev], ws,
+                     ws + (size_t)B * H_q * N_q * plan.splits * d,
+                     paged ? table : nullptr, max_blocks, paged ? log2_of(block_size) : 0,
+                     num_blocks};
   return attn::launch_decode(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+// Checks the paged sizes and returns N_kv = max_blocks * block_size, or -1.
+int64_t paged_capacity(int max_blocks, int block_size, int num_blocks) {
+  if (max_blocks < 0 || num_blocks < 0) return -1;
+  if (!valid_block_size(block_size)) return -2;
+  const int64_t n = (int64_t)max_blocks * block_size;
+  return n > (1LL << 30) ? -1 : n;
+}
+
+}  // namespace
+
+int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
+                    void* o, float* lse, int B, int H_q, int H_kv, int N_q, int N_kv, int d,
+                    int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  const size_t nkv =
+      (B > 0 && H_kv > 0 && N_kv > 0 && d > 0) ? (size_t)B * H_kv * N_kv * d * elem_size(dtype) : 0;
+  return decode_launch(q, k_cache, v_cache, nkv, nullptr, 0, 0, 0, kv_lens, o, lse, B, H_q, H_kv,
+                       N_q, N_kv, d, causal, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+size_t attn_decode_paged_workspace_size(int B, int H_q, int H_kv, int N_q, int max_blocks,
+                                        int block_size, int d, int dtype) {
+  const int64_t n = paged_capacity(max_blocks, block_size, 1);
+  if (n < 0) return 0;
+  if (check_common(B, H_q, H_kv, N_q, (int)n, d, dtype, 1.f) != ATTN_OK) return 0;
+  if (N_q < 1 || N_q > attn::kDecodeMaxNq) return 0;
+  return attn::decode_plan(B, H_q, H_kv, N_q, (int)n, d, true).workspace_bytes;
+}
+
+int attn_decode_paged_fwd(const void* q, const void* k_pool, const void* v_pool,
+                          const int* block_table, const int* kv_lens, void* o, float* lse, int B,
+                          int H_q, int H_kv, int N_q, int max_blocks, int block_size,
+                          int num_blocks, int d, int causal, float scale, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const int64_t n = paged_capacity(max_blocks, block_size, num_blocks);
+  if (n == -2) return ATTN_ERR_UNSUPPORTED;
+  if (n < 0) return ATTN_ERR_SHAPE;
+  const size_t npool = (num_blocks > 0 && H_kv > 0 && d > 0)
+                           ? (size_t)num_blocks * H_kv * block_size * d * 2
+                           : 0;
+  return decode_launch(q, k_pool, v_pool, npool, block_table, max_blocks, block_size, num_blocks,
+                       kv_lens, o, lse, B, H_q, H_kv, N_q, (int)n, d, causal, scale, dtype,
+                       workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -39,6 +39,12 @@ struct DecodeArgs {
   int num_cus; // compute units of the device (sizes the persistent grid)
   float* part_u;   // [B, H_q, N_q, splits, d] un-normalised partial outputs
   float* part_ml;  // [B, H_q, N_q, splits, 2] partial (max in log2 units, denominator)
+  // paged caches (block_table non-null): k and v are pools
+  // [num_blocks, H_kv, block_size, d]; N_kv = max_blocks * block_size
+  const int* block_table;  // [B, max_blocks]
+  int max_blocks;
+  int block_size_log2;
+  int num_blocks;
 };
 
 // Split plan shared by the workspace query and the launch.
@@ -47,7 +53,7 @@ struct DecodePlan {
   int splits;
   size_t workspace_bytes;
 };
-DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d);
+DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool paged);
 constexpr int kDecodeMaxNq = 64;  // query tokens per request the decode path takes
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

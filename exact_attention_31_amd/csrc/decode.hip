@@ -46,37 +46,95 @@ template <int D> struct DecLds {
   static constexpr int kV = 4 * kWaveKeys * VST;  // V staging, 4 wavefronts (elements)
 };
 
+// Where one request's cached rows live. Contiguous caches are
+// [B, H_kv, N_kv, d]. Paged caches are a pool of fixed-size blocks
+// [num_blocks, H_kv, block_size, d] plus a per-request block table
+// [B, max_blocks] that maps logical block i (positions i*block_size ..
+// (i+1)*block_size - 1) to a physical block of the pool.
+struct KvSrc {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int* table;     // paged only
+  int max_blocks;       // paged only: table row length
+  int bs_log2;          // paged only: log2(block_size), block_size >= 16
+  int num_blocks;       // paged only: pool size in blocks
+};
+
+struct SplitParams {
+  const uint16_t* q;
+  KvSrc kv;
+  const int* kv_lens;
+  float* part_u;
+  float* part_ml;
+  int B, H_q, H_kv, N_q, N_kv, causal, splits, chunk;
+  float scale_log2;
+};
+
 // One work unit, done by one wavefront alone: keys [split*chunk,
 // min((split+1)*chunk, len)) of request b for KV head hk and query column
 // groups NG*qg .. NG*qg + NG-1 (16 columns each). Writes that chunk's partial
 // (u, m, l) for the groups' query rows. The NG groups share every K register
 // and every V operand read from LDS; only the matrix products are per group.
-template <class TT, int D, int NG>
-__device__ __forceinline__ void wave_unit(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    float* __restrict__ part_u, float* __restrict__ part_ml, int H_q, int H_kv, int N_q, int N_kv,
-    int causal, int splits, int chunk, float scale_log2, int b, int hk, int qg, int split, int len,
-    uint16_t* sV) {
+template <class TT, int D, int NG, bool PAGED>
+__device__ __forceinline__ void wave_unit(const SplitParams& P, int b, int hk, int qg, int split,
+                                          int len, uint16_t* sV) {
   constexpr int VST = DecLds<D>::VST;
   constexpr int KS = D / 32;        // k-steps of the score MFMA
   constexpr int DB = D / 16;        // 16-wide output blocks
   constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int VL = kWaveKeys * CPR / 64;  // V loads per lane per step
+  constexpr int VL = kWaveKeys * CPR / 64;  // V loads per lane per step (half per 16 rows)
 
   const int lane = threadIdx.x & 63;
-  const int c16 = lane & 15;   // query column (S^T) / output head
+  const int c16 = lane & 15;   // query column (S^T) / output row
   const int g = lane >> 4;     // 16-lane group
-  const int G = H_q / H_kv;
-  const int wbeg = split * chunk;
-  const int wend = min(wbeg + chunk, len);
+  const int H_kv = P.H_kv, N_q = P.N_q;
+  const int G = P.H_q / H_kv;
+  const int wbeg = split * P.chunk;
+  const int wend = min(wbeg + P.chunk, len);
   const int nsteps = (wend - wbeg + kWaveKeys - 1) / kWaveKeys;
+  const float scale_log2 = P.scale_log2;
 
-  // this KV head's cache rows; rows past the request's length read as zeros
-  const uint16_t* Kh = K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
-  const uint16_t* Vh = V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D;
+  // ---- cache addressing. rows16(r0) is a buffer resource over rows r0 ..
+  // r0 + 15 of this request and KV head (r0 a multiple of 16) bounded by the
+  // request's length: rows past it read as zeros.
+  const uint16_t* Kh = nullptr;
+  const uint16_t* Vh = nullptr;
+  int tb0 = -1, tb1 = -1, blk0 = 0;
+  if constexpr (!PAGED) {
+    Kh = P.kv.k + ((int64_t)b * H_kv + hk) * (int64_t)P.N_kv * D;
+    Vh = P.kv.v + ((int64_t)b * H_kv + hk) * (int64_t)P.N_kv * D;
+  } else {
+    // this chunk's block-table entries, one per lane (a chunk spans at most
+    // 128 blocks); entries of blocks past the request's length are not read
+    const int bsl = P.kv.bs_log2;
+    blk0 = wbeg >> bsl;
+    const int nblk = (len + (1 << bsl) - 1) >> bsl;
+    const int* trow = P.kv.table + (int64_t)b * P.kv.max_blocks;
+    if (blk0 + lane < nblk) tb0 = trow[blk0 + lane];
+    if (blk0 + 64 + lane < nblk) tb1 = trow[blk0 + 64 + lane];
+  }
+  auto rows16 = [&](const uint16_t* base, int r0) {
+    if constexpr (!PAGED) {
+      const int n = max(0, len - r0);
+      return buffer_rsrc(base + (int64_t)min(r0, len) * D, (uint32_t)n * D * 2);
+    } else {
+      const int bsl = P.kv.bs_log2;
+      const int li = (r0 >> bsl) - blk0;   // wavefront-uniform
+      const int pb = li < 64 ? __builtin_amdgcn_readlane(tb0, li) : __builtin_amdgcn_readlane(tb1, li - 64);
+      const int off = r0 & ((1 << bsl) - 1);
+      // a table entry outside the pool reads as zeros instead of faulting
+      const bool ok = (unsigned)pb < (unsigned)P.kv.num_blocks && r0 < len;
+      const int n = ok ? min((1 << bsl) - off, len - r0) : 0;
+      const int64_t row = ok ? (((int64_t)pb * H_kv + hk) << bsl) + off : 0;
+      return buffer_rsrc(base + row * D, (uint32_t)n * D * 2);
+    }
+  };
+  const uint16_t* kbase = PAGED ? P.kv.k : Kh;
+  const uint16_t* vbase = PAGED ? P.kv.v : Vh;
+
   // The G query heads of KV head hk, N_q query rows each, are G*N_q contiguous
-  // rows of Q; they are the MFMA's query columns, 16 per group qg.
-  const int64_t qrow0 = ((int64_t)b * H_q + (int64_t)hk * G) * N_q;  // first row of the KV head's block
+  // rows of Q; they are the MFMA's query columns, 16 per group.
+  const int64_t qrow0 = ((int64_t)b * P.H_q + (int64_t)hk * G) * N_q;  // first row of the KV head's block
   int col0[NG], ncols[NG], lim[NG];
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
@@ -85,7 +143,7 @@ __device__ __forceinline__ void wave_unit(
     // keys below lim are visible to this lane's column (query row i = col % N_q,
     // aligned so that the last query row sees the last key)
     const int qi = (col0[j] + c16) % N_q;
-    lim[j] = causal ? min(len, len - N_q + qi + 1) : len;
+    lim[j] = P.causal ? min(len, len - N_q + qi + 1) : len;
   }
 
   // Q^T operands: column c16 of group j = row col0[j] + c16 of the block,
@@ -93,7 +151,7 @@ __device__ __forceinline__ void wave_unit(
   u32x4_t qreg[NG][KS];
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
-    const auto rQ = buffer_rsrc(Q + (qrow0 + min(col0[j], G * N_q)) * D, (uint32_t)ncols[j] * D * 2);
+    const auto rQ = buffer_rsrc(P.q + (qrow0 + min(col0[j], G * N_q)) * D, (uint32_t)ncols[j] * D * 2);
 #pragma unroll
     for (int st = 0; st < KS; ++st)
       qreg[j][st] = buffer_load16(rQ, (uint32_t)(c16 * D + 32 * st + 8 * g) * 2);
@@ -111,26 +169,23 @@ __device__ __forceinline__ void wave_unit(
     l[j] = 0.f;
   }
 
-  // K rows feed the A operand directly: key = w0 + 16*kb + c16, d = 32*st + 8*g
-  // V rows: lane takes 16-byte chunk c = lane + 64*i of the step's rows
-  // (row c / CPR, column c % CPR). Each step's loads use a resource based at
-  // its first row (wavefront-uniform, in scalar registers) and bounded by the
-  // request's length, so the per-lane offsets stay fixed across steps.
-  const uint32_t koff0 = (uint32_t)(c16 * D + 8 * g) * 2;
-  const uint32_t koff1 = koff0 + 16 * D * 2;
+  // K rows feed the A operand directly: key = w0 + 16*kb + c16, d = 32*st + 8*g.
+  // V rows: lane takes 16-byte chunk c = lane + 64*i of the step's rows (row
+  // c / CPR, column c % CPR); the first VL/2 chunks are rows 0..15. The lane
+  // offsets are fixed; each 16-row half has its own wavefront-uniform resource.
+  const uint32_t koff = (uint32_t)(c16 * D + 8 * g) * 2;
   const uint32_t voff = (uint32_t)lane * 16;
   u32x4_t ka[2][2][KS], va[2][VL];
   auto issue = [&](int w0, u32x4_t (&kk)[2][KS], u32x4_t (&vv)[VL]) {
-    const uint32_t rest = (uint32_t)(len - w0) * D * 2;  // w0 < len
-    const auto rK = buffer_rsrc(Kh + (int64_t)w0 * D, rest);
-    const auto rV = buffer_rsrc(Vh + (int64_t)w0 * D, rest);
 #pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      kk[0][st] = buffer_load16(rK, koff0 + 64 * st);
-      kk[1][st] = buffer_load16(rK, koff1 + 64 * st);
+    for (int h = 0; h < 2; ++h) {
+      const auto rK = rows16(kbase, w0 + 16 * h);
+      const auto rV = rows16(vbase, w0 + 16 * h);
+#pragma unroll
+      for (int st = 0; st < KS; ++st) kk[h][st] = buffer_load16(rK, koff + 64 * st);
+#pragma unroll
+      for (int i = 0; i < VL / 2; ++i) vv[h * (VL / 2) + i] = buffer_load16(rV, voff + 1024 * i);
     }
-#pragma unroll
-    for (int i = 0; i < VL; ++i) vv[i] = buffer_load16(rV, voff + 1024 * i);
   };
   auto step = [&](int w0, const u32x4_t (&kk)[2][KS], const u32x4_t (&vv)[VL]) {
 #pragma unroll
@@ -216,14 +271,14 @@ __device__ __forceinline__ void wave_unit(
     float lj = l[j] + __shfl_xor(l[j], 16);
     lj = half_sum(lj);
     if (c16 < ncols[j]) {
-      const int64_t row = (qrow0 + col0[j] + c16) * splits + split;
-      float* pu = part_u + row * D;
+      const int64_t row = (qrow0 + col0[j] + c16) * P.splits + split;
+      float* pu = P.part_u + row * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         *(f32x4_t*)(pu + 16 * db + 4 * g) = oacc[j][db];
       if (g == 0) {
-        part_ml[row * 2 + 0] = m[j];
-        part_ml[row * 2 + 1] = lj;
+        P.part_ml[row * 2 + 0] = m[j];
+        P.part_ml[row * 2 + 1] = lj;
       }
     }
   }
@@ -236,22 +291,19 @@ __device__ __forceinline__ void wave_unit(
 // handing units out round-robin to the wavefronts of the grid balances ragged
 // lengths without atomics or barriers. Each wavefront walks the requests
 // forward as its unit index grows, reading kv_lens as it goes.
-template <class TT, int D, int NG, int OCC>
-__global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const int* __restrict__ kv_lens, float* __restrict__ part_u, float* __restrict__ part_ml,
-    int B, int H_q, int H_kv, int N_q, int N_kv, int causal, int splits, int chunk,
-    float scale_log2) {
+template <class TT, int D, int NG, int OCC, bool PAGED>
+__global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(const SplitParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[DecLds<D>::kV];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   uint16_t* sV = smem + wave * kWaveKeys * DecLds<D>::VST;
-  const int G = H_q / H_kv;
-  const int ngroups = (G * N_q + NG * kQCols - 1) / (NG * kQCols);  // units of NG column groups
-  const int HG = H_kv * ngroups;
+  const int G = P.H_q / P.H_kv;
+  const int ngroups = (G * P.N_q + NG * kQCols - 1) / (NG * kQCols);  // units of NG column groups
+  const int HG = P.H_kv * ngroups;
   const int nw = (int)gridDim.x * 4;
+  const int B = P.B, chunk = P.chunk;
   auto len_of = [&](int b) {
-    const int n = kv_lens ? kv_lens[b] : N_kv;
-    return min(max(n, 0), N_kv);
+    const int n = P.kv_lens ? P.kv_lens[b] : P.N_kv;
+    return min(max(n, 0), P.N_kv);
   };
   int cb = 0;                 // request holding the current global chunk
   int cstart = 0;             // its first global chunk index
@@ -268,8 +320,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(
       }
     }
     if (cb >= B) break;
-    wave_unit<TT, D, NG>(Q, K, V, part_u, part_ml, H_q, H_kv, N_q, N_kv, causal, splits, chunk,
-                     scale_log2, cb, hg / ngroups, hg - (hg / ngroups) * ngroups, c - cstart, lb, sV);
+    wave_unit<TT, D, NG, PAGED>(P, cb, hg / ngroups, hg - (hg / ngroups) * ngroups, c - cstart, lb, sV);
   }
 }
 
@@ -348,10 +399,26 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   const int64_t slots = (int64_t)OCC * (a.num_cus > 0 ? a.num_cus : 256);  // workgroups of 4 wavefronts
   const int64_t wgs = (units + 3) / 4;
   dim3 grid((unsigned)(wgs < slots ? wgs : slots));
-  hipLaunchKernelGGL((decode_split_kernel<TT, D, NG, OCC>), grid, dim3(kThreads), 0, st,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.kv_lens,
-                     a.part_u, a.part_ml, a.B, a.H_q, a.H_kv, a.N_q, a.N_kv, a.causal, a.splits,
-                     a.chunk, a.scale * kLog2e);
+  SplitParams P;
+  P.q = (const uint16_t*)a.q;
+  P.kv = KvSrc{(const uint16_t*)a.k, (const uint16_t*)a.v, a.block_table, a.max_blocks,
+               a.block_size_log2, a.num_blocks};
+  P.kv_lens = a.kv_lens;
+  P.part_u = a.part_u;
+  P.part_ml = a.part_ml;
+  P.B = a.B;
+  P.H_q = a.H_q;
+  P.H_kv = a.H_kv;
+  P.N_q = a.N_q;
+  P.N_kv = a.N_kv;
+  P.causal = a.causal;
+  P.splits = a.splits;
+  P.chunk = a.chunk;
+  P.scale_log2 = a.scale * kLog2e;
+  if (a.block_table != nullptr)
+    hipLaunchKernelGGL((decode_split_kernel<TT, D, NG, OCC, true>), grid, dim3(kThreads), 0, st, P);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<TT, D, NG, OCC, false>), grid, dim3(kThreads), 0, st, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int BH = a.B * a.H_q * a.N_q;
@@ -361,36 +428,11 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d) {
-  const int G = H_q / H_kv;
-  const int64_t units = (int64_t)B * H_kv * ((G * N_q + kQCols - 1) / kQCols);
-  (void)units;
-  // The persistent kernel hands chunks out round-robin to wavefronts. Chunks of
-  // up to 2048 keys (1 MB of K and V at d = 128) keep ragged lengths balanced
-  // while each wavefront's start-up latency (query and first K/V loads) stays
-  // a few percent of its chunk; short caches use chunks of at least 128 keys.
-  int64_t chunk = ((int64_t)N_kv + 15) / 16;
-  chunk = ((chunk + kWaveKeys * 4 - 1) / (kWaveKeys * 4)) * (kWaveKeys * 4);
-  if (chunk < 128) chunk = 128;
-  if (chunk > 2048) chunk = 2048;
-  // tuning override (keys per split, rounded up to a multiple of 128)
-  if (const char* e = getenv("ATTN_DECODE_CHUNK")) {
-    const long v = strtol(e, nullptr, 10);
-    if (v > 0 && v <= (1L << 24)) chunk = ((v + kStepKeys - 1) / kStepKeys) * kStepKeys;
-  }
-  DecodePlan p;
-  p.chunk = (int)chunk;
-  p.splits = N_kv > 0 ? (int)((N_kv + chunk - 1) / chunk) : 1;
-  p.workspace_bytes = (size_t)B * H_q * N_q * p.splits * (size_t)(d + 2) * sizeof(float);
-  return p;
-}
-
 template <class TT>
 hipError_t launch_dtype(const DecodeArgs& a, hipStream_t st) {
-  // more than 16 query rows per KV head: each wavefront serves two column
-  // groups, so K and V are read once per 32 rows (ATTN_DECODE_GROUPS=1 forces one)
+  // more than 16 query rows per KV head: each wavefront serves two or four
+  // column groups, so K and V are read once per 32 or 64 rows
+  // (ATTN_DECODE_GROUPS = 1, 2 or 4 forces a choice)
   const int cols = (a.H_q / a.H_kv) * a.N_q;
   int ng = cols <= kQCols ? 1 : (cols <= 2 * kQCols ? 2 : 4);
   if (const char* e = getenv("ATTN_DECODE_GROUPS")) {
@@ -403,6 +445,32 @@ hipError_t launch_dtype(const DecodeArgs& a, hipStream_t st) {
   }
   if (ng == 1) return launch_t<TT, 128, 1, 2>(a, st);
   return ng == 2 ? launch_t<TT, 128, 2, 1>(a, st) : launch_t<TT, 128, 4, 1>(a, st);
+}
+
+}  // namespace
+
+DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool paged) {
+  // The persistent kernel hands chunks out round-robin to wavefronts. Chunks of
+  // up to 2048 keys (1 MB of K and V at d = 128) keep ragged lengths balanced
+  // while each wavefront's start-up latency (query and first K/V loads) stays
+  // a few percent of its chunk; short caches use chunks of at least 128 keys.
+  int64_t chunk = ((int64_t)N_kv + 15) / 16;
+  chunk = ((chunk + kWaveKeys * 4 - 1) / (kWaveKeys * 4)) * (kWaveKeys * 4);
+  if (chunk < 128) chunk = 128;
+  if (chunk > 2048) chunk = 2048;
+  // tuning override (keys per split, rounded up to a multiple of 128; at most
+  // 2048 for paged caches, whose chunks keep their block-table entries in one
+  // register pair per lane)
+  if (const char* e = getenv("ATTN_DECODE_CHUNK")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v > 0 && v <= (1L << 24)) chunk = ((v + kStepKeys - 1) / kStepKeys) * kStepKeys;
+    if (paged && chunk > 2048) chunk = 2048;
+  }
+  DecodePlan p;
+  p.chunk = (int)chunk;
+  p.splits = N_kv > 0 ? (int)((N_kv + chunk - 1) / chunk) : 1;
+  p.workspace_bytes = (size_t)B * H_q * N_q * p.splits * (size_t)(d + 2) * sizeof(float);
+  return p;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {

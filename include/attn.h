@@ -105,6 +105,38 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, con
                     int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/*
+ * Bytes of device workspace attn_decode_paged_fwd needs (0 if the sizes are
+ * invalid). A pure function of its arguments.
+ */
+size_t attn_decode_paged_workspace_size(int B, int H_q, int H_kv, int N_q, int max_blocks,
+                                        int block_size, int d, int dtype);
+
+/*
+ * Decode forward over a paged (block-wise) KV cache: the cache is cut into
+ * fixed-size blocks that requests take from one shared pool, which removes the
+ * fragmentation of per-request contiguous buffers (papanda925.com survey,
+ * block-wise KV cache management in its recent-trends and method sections).
+ * Same computation, partial/merge scheme and query layout as attn_decode_fwd.
+ *   k_pool/v_pool [num_blocks, H_kv, block_size, d] (dtype), shared by all
+ *     requests: block p holds block_size consecutive positions of every KV head;
+ *   block_table: device int32 [B, max_blocks]; entry (b, i) is the pool block
+ *     holding positions i*block_size .. (i+1)*block_size - 1 of request b. Only
+ *     the entries of blocks below kv_lens[b] are read. An entry outside
+ *     [0, num_blocks) reads as zero keys and values (the request's result is
+ *     then meaningless, but nothing outside the pool is touched);
+ *   kv_lens: device int32 [B] or NULL; clamped to [0, max_blocks * block_size];
+ *   block_size: a power of two in [16, 4096] (else ATTN_ERR_UNSUPPORTED);
+ *   q, o, lse, causal, scale, dtype, N_q, workspace: as for attn_decode_fwd,
+ *     with attn_decode_paged_workspace_size(...) bytes of workspace.
+ * Work: 2 * kv_lens[b] * H_kv * d * sizeof(dtype) bytes of K and V read.
+ */
+int attn_decode_paged_fwd(const void* q, const void* k_pool, const void* v_pool,
+                          const int* block_table, const int* kv_lens, void* o, float* lse, int B,
+                          int H_q, int H_kv, int N_q, int max_blocks, int block_size,
+                          int num_blocks, int d, int causal, float scale, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_string(int status);
 

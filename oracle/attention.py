@@ -31,6 +31,11 @@ What it computes (the plain definition, written out):
 * A row with no visible key has output 0 and log-sum-exp -inf.
 * lse = m + ln(l), the per-row statistics that the backward pass keeps
   (marketmaker.cc, "Rückwärtsdurchlauf").
+* A paged (block-wise) KV cache stores fixed-size blocks in one shared pool
+  and maps each request's logical blocks to pool blocks (papanda925.com survey,
+  "Block-wise KV Cache" in its recent-trends and method sections). Attention
+  over it is attention over the cache that the block table describes: gather
+  the blocks into a contiguous cache, then apply the definition above.
 
 All arithmetic is float64 on the exact (dtype-rounded) input values; numpy's
 matmul (BLAS dgemm) forms the score rows and the weighted sum.
@@ -155,6 +160,33 @@ def attention_head_rows(q_rows, rows, N_q: int, k_head, v_head, causal: bool, sc
     return _head(q_rows, rows, N_q, k_head, v_head, causal, scale, n, 256)
 
 
+def gather_paged(pool, block_table, lens, block_size: int):
+    """The contiguous cache [B, H_kv, max_blocks * block_size, d] that a paged
+    cache describes. pool: [num_blocks, H_kv, block_size, d]; block_table
+    [B, max_blocks] maps logical block i of request b to a pool block; only
+    the blocks holding positions below lens[b] are read (the rest stay 0)."""
+    pool = np.asarray(pool)
+    table = np.asarray(block_table)
+    B, max_blocks = table.shape
+    _, H_kv, bs, d = pool.shape
+    if bs != block_size:
+        raise ValueError("pool block size mismatch")
+    out = np.zeros((B, H_kv, max_blocks * bs, d), dtype=pool.dtype)
+    for b in range(B):
+        n = int(lens[b])
+        for i in range((n + bs - 1) // bs):
+            out[b, :, i * bs:(i + 1) * bs] = pool[int(table[b, i])]
+    return out
+
+
+def attention_paged_ref(q, k_pool, v_pool, block_table, kv_lens, block_size: int, causal: bool,
+                        scale: float):
+    """Exact attention over a paged KV cache: attention_ref on the gathered cache."""
+    k = gather_paged(k_pool, block_table, kv_lens, block_size)
+    v = gather_paged(v_pool, block_table, kv_lens, block_size)
+    return attention_ref(q, k, v, causal, scale, kv_lens=kv_lens)
+
+
 def softmax_weights(scores: np.ndarray) -> np.ndarray:
     """Row softmax of a score matrix (-inf entries get weight 0), float64, two-pass."""
     s = np.asarray(scores, dtype=np.float64)
@@ -170,4 +202,5 @@ def attention_flops(N_q: int, n: int, d: int, causal: bool) -> int:
 
 
 __all__ = ["score_bytes", "kv_cache_bytes", "visible_pairs", "attention_ref", "attention_head_rows",
+           "gather_paged", "attention_paged_ref",
            "softmax_weights", "attention_flops", "MiB"]

@@ -104,3 +104,36 @@ def test_decode_argument_errors():
     assert df(Hq=12, Hkv=8) == 3
     assert df(ws=FAKE[1]) == 8       # workspace overlaps the K cache
     assert df() in (7,)              # valid: reaches the (absent) device
+
+
+def pws(B=2, Hq=8, Hkv=1, Nq=1, maxb=64, bs=16, d=128, dtype=E.ATTN_BF16):
+    return L.attn_decode_paged_workspace_size(B, Hq, Hkv, Nq, maxb, bs, d, dtype)
+
+
+def pdf(ws=P(0x7000000000), wsb=None, table=P(0x7800000000), Nq=1, dtype=E.ATTN_BF16, **kw):
+    a = dict(B=2, Hq=8, Hkv=1, maxb=64, bs=16, nblk=100, d=128)
+    a.update(kw)
+    if wsb is None:
+        wsb = pws(a["B"], a["Hq"], a["Hkv"], Nq, a["maxb"], a["bs"], a["d"], dtype)
+    return L.attn_decode_paged_fwd(FAKE[0], FAKE[1], FAKE[2], table, None, FAKE[3], None, a["B"],
+                                   a["Hq"], a["Hkv"], Nq, a["maxb"], a["bs"], a["nblk"], a["d"], 0,
+                                   0.088, dtype, ws, wsb, None)
+
+
+def test_paged_decode_workspace_size_matches_contiguous_capacity():
+    # a paged cache of max_blocks * block_size positions splits like a
+    # contiguous cache of that capacity
+    assert pws() == ws_size(Nkv=64 * 16) > 0
+    assert pws(maxb=10, bs=256, Nq=3) == ws_size(Nkv=2560, Nq=3)
+    assert pws(bs=24) == 0 and pws(bs=8) == 0 and pws(bs=8192) == 0 and pws(maxb=-1) == 0
+
+
+def test_paged_decode_argument_errors():
+    assert pdf(bs=48) == 4 and pdf(bs=8) == 4 and pdf(dtype=E.ATTN_F32) == 4 and pdf(Nq=65) == 4
+    assert pdf(table=None) == 1
+    assert pdf(maxb=-1) == 2 and pdf(nblk=-5) == 2
+    assert pdf(ws=None) == 5 and pdf(wsb=8) == 5
+    assert pdf(Hq=12, Hkv=8) == 3
+    assert pdf(table=FAKE[3]) == 8   # block table overlaps the output
+    assert pdf(B=0) == 0
+    assert pdf() == 7 and pdf(bs=4096, maxb=3) == 7 and pdf(nblk=0) == 7
