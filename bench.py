@@ -11,6 +11,8 @@ Default run (one JSON line on stdout):
     stream) to the bf16 MFMA peak; "decode_roofline" relates decode to HBM peak;
   * "decode_multi_token" times the same caches with 4 new tokens per request
     (causal, bottom-right aligned), as a speculative-decoding verifier sees it;
+  * "decode_paged" times the same caches cut into 16-position blocks scattered
+    over a pool and read through a block table;
   * "cpu_baseline" times the float64 oracle on a bounded sample of the prefill
     workload on this host's cores.
 `--all` also times the other three workloads (fp32 single head, the 23,400-step
@@ -154,6 +156,44 @@ def bench_decode(cfg, steps, warmup, torch, E, ragged=False, cache=None):
             "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12, "wall_s": wall}, cache
 
 
+def bench_decode_paged(cfg, steps, warmup, torch, E, cache, block_size=16):
+    """Decode over a paged copy of `cache`: its 16-position blocks are scattered
+    over a pool in a seeded random order and addressed through a block table."""
+    import attn_inputs as A
+    k, v = cache
+    B, H_kv, N, d = k.shape
+    nb = N // block_size
+    lens = np.full(B, N, np.int32)
+    table, nblk = A.paged_layout(lens, block_size, nb, seed=5)
+    perm = torch.from_numpy(table.reshape(-1).astype(np.int64)).cuda()
+    kp = torch.empty((nblk, H_kv, block_size, d), dtype=k.dtype, device="cuda")
+    vp = torch.empty_like(kp)
+    kp[perm] = k.reshape(B, H_kv, nb, block_size, d).permute(0, 2, 1, 3, 4).reshape(-1, H_kv, block_size, d)
+    vp[perm] = v.reshape(B, H_kv, nb, block_size, d).permute(0, 2, 1, 3, 4).reshape(-1, H_kv, block_size, d)
+    table_d = torch.from_numpy(table).cuda()
+    q = make_device_tensor(cfg, "q", torch)
+    o = torch.empty_like(q)
+    lens_d = torch.from_numpy(lens).cuda()
+    ws = torch.empty(E.attn_decode_paged_workspace_size(B, cfg.H_q, H_kv, cfg.N_q, nb, block_size, d,
+                                                        q.dtype), dtype=torch.uint8, device="cuda")
+
+    def call():
+        E.attn_decode_paged_fwd(q, kp, vp, table_d, o, kv_lens=lens_d, scale=cfg.scale,
+                                causal=cfg.causal, workspace=ws)
+
+    ms, wall = time_launches(call, steps, warmup, torch)
+    # the same logical cache through the contiguous path gives the same bits
+    oc = E.attn_decode_fwd(q, k, v, kv_lens=lens_d, scale=cfg.scale, causal=cfg.causal)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o, oc))
+    nbytes = decode_kv_bytes(cfg, lens)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del kp, vp, q, o, ws, oc
+    return {"config": f"{cfg.cid}-paged{block_size}", "name": cfg.name + f", paged, block {block_size}",
+            "ms": ms, "kv_bytes": nbytes, "gb_per_s": gbs, "frac_of_peak": gbs / PEAK_HBM,
+            "peak_gb_per_s": PEAK_HBM, "wall_s": wall, "equals_contiguous": same}
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=3):
     """A plain device-to-device copy of known size (torch's copy kernel): the
     HBM counters read for it calibrate the FETCH_SIZE / WRITE_SIZE scale."""
@@ -225,8 +265,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--all", action="store_true", help="also time configs 1, 3, 4 and ragged decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "decode_ragged", "decode_multi"],
-                    default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_ragged", "decode_multi",
+                                       "decode_paged"], default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for HBM counter calibration)")
@@ -264,6 +304,15 @@ def main(argv=None):
               f"{r['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         res["decode_multi"] = r
         if args.only == "decode_multi":
+            res["decode"] = r
+    if args.only in (None, "decode_paged"):
+        if cache is None:
+            _, cache = bench_decode(A.CONFIGS[5], 1, 1, torch, E)
+        r = bench_decode_paged(A.CONFIGS[5], args.steps, args.warmup, torch, E, cache)
+        print(f"# decode c5 paged (block 16): {r['ms']:.3f} ms  {r['gb_per_s']:.0f} GB/s  "
+              f"same bits as contiguous: {r['equals_contiguous']}", file=sys.stderr, flush=True)
+        res["decode_paged"] = r
+        if args.only == "decode_paged":
             res["decode"] = r
     extra = []
     if args.only == "decode_ragged":
@@ -325,6 +374,15 @@ def main(argv=None):
             "ms_per_step": round(dm["ms"], 5), "value": round(dm["gb_per_s"], 2), "unit": "GB/s",
             "frac_of_hbm_peak": round(dm["frac_of_peak"], 4), "tflops": round(dm["tflops"], 2),
             "kernel": "decode_split_kernel + decode_merge_kernel (one step)"}
+    dp = res.get("decode_paged")
+    if dp and dp is not d:
+        line["decode_paged"] = {
+            "workload": "GQA decode over a paged cache (16-position blocks scattered over a pool "
+                        "in random order), bf16, B=64, H_q=32, H_kv=4, d=128, KV 32768 per request",
+            "ms_per_step": round(dp["ms"], 5), "value": round(dp["gb_per_s"], 2), "unit": "GB/s",
+            "frac_of_hbm_peak": round(dp["frac_of_peak"], 4),
+            "equals_contiguous": dp["equals_contiguous"],
+            "kernel": "decode_split_kernel<paged> + decode_merge_kernel (one step)"}
     if p:
         line["prefill_first_call_ms"] = round(p["first_call_ms"], 3)
     if cpu:
