@@ -17,9 +17,12 @@ to bf16/fp16 on the device side are both exact):
 
 tensor ids: Q=0, K=1, V=2; ragged decode lengths use SeedSequence([31, cfg, 3]).
 Paged-cache block tables are a seeded permutation of the pool's blocks,
-SeedSequence([31, 2000, seed]).
+SeedSequence([31, 2000, seed]). FP8 caches are E4M3 codes of sigma * N(0, 1)
+divided by a per-tensor scale, SeedSequence([31, 3000, seed]), rounded by
+torch's float8_e4m3fn cast.
 """
 from .configs import CONFIGS, Config, get_config, ragged_lengths  # noqa: F401
 from .gen import (  # noqa: F401
     bf16_round, fp16_round, round_to_dtype, slice_values, tensor_values, random_tensor, paged_layout,
+    fp8_codes,
 )

@@ -94,3 +94,13 @@ def paged_layout(lens, block_size: int, max_blocks: int, seed: int, spare: int =
         table[b, :n] = perm[pos:pos + n]
         pos += n
     return table, num_blocks
+
+
+def fp8_codes(shape, seed: int, scale: float, sigma: float = 1.0) -> np.ndarray:
+    """Seeded FP8 E4M3 cache codes (uint8) for values sigma * N(0, 1) stored with a
+    per-tensor dequantisation scale: codes = E4M3(x / scale), rounded to nearest
+    even by torch's float8_e4m3fn cast (magnitudes are clipped to 448 first)."""
+    import torch
+    x = _rng(31, 3000, seed).standard_normal(shape, dtype=np.float32) * np.float32(sigma)
+    y = np.clip(x / np.float32(scale), -448.0, 448.0).astype(np.float32)
+    return torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()

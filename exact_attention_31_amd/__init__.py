@@ -54,6 +54,12 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_paged_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i,
                                           vp, sz, vp]
     lib.attn_decode_paged_fwd.restype = i
+    lib.attn_decode_fp8_fwd.argtypes = [vp, vp, vp, f, f, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz,
+                                        vp]
+    lib.attn_decode_fp8_fwd.restype = i
+    lib.attn_decode_paged_fp8_fwd.argtypes = [vp, vp, vp, f, f, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                              i, f, i, vp, sz, vp]
+    lib.attn_decode_paged_fp8_fwd.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -235,6 +241,110 @@ def attn_decode_paged_fwd(q, k_pool, v_pool, block_table, o=None, *, kv_lens=Non
     return (o, lse) if (return_lse or lse is not None) else o
 
 
+_FP8 = getattr(torch, "float8_e4m3fn", None)
+
+
+def _codes(name, t, dev, ndim=4):
+    """FP8 E4M3 caches as uint8 codes (a float8_e4m3fn tensor is viewed as its bytes)."""
+    if isinstance(t, torch.Tensor) and _FP8 is not None and t.dtype == _FP8:
+        t = t.view(torch.uint8)
+    _check_tensor(name, t, torch.uint8, dev, ndim=ndim)
+    return t
+
+
+def attn_decode_fp8_fwd(q, k_cache, v_cache, k_scale: float, v_scale: float, o=None, *,
+                        kv_lens=None, lse=None, causal: bool = False, scale: float | None = None,
+                        workspace=None, return_lse: bool = False, stream=None):
+    """Decode over an FP8 E4M3 cache: q bf16 [B,H_q,N_q,d]; k/v_cache uint8 (or
+    float8_e4m3fn) [B,H_kv,N_kv,d] holding codes; values = code * k_scale / v_scale."""
+    lib = load()
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, dev)
+    k_cache = _codes("k_cache", k_cache, dev)
+    v_cache = _codes("v_cache", v_cache, dev)
+    B, H_q, N_q, d = q.shape
+    _, H_kv, N_kv, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, H_kv, N_kv, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if kv_lens is not None:
+        _check_tensor("kv_lens", kv_lens, torch.int32, dev, ndim=1)
+        if kv_lens.shape[0] != B:
+            raise ValueError("kv_lens must have B entries")
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor("o", o, q.dtype, dev)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, dev, ndim=3)
+    need = attn_decode_workspace_size(B, H_q, H_kv, N_q, N_kv, d, ATTN_BF16)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(dev):
+        st = lib.attn_decode_fp8_fwd(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale),
+                                     float(v_scale), _ptr(kv_lens), _ptr(o), _ptr(lse), B, H_q, H_kv,
+                                     N_q, N_kv, d, int(bool(causal)), float(scale), ATTN_BF16,
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(dev, stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_fp8_fwd")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_decode_paged_fp8_fwd(q, k_pool, v_pool, k_scale: float, v_scale: float, block_table,
+                              o=None, *, kv_lens=None, lse=None, causal: bool = False,
+                              scale: float | None = None, workspace=None, return_lse: bool = False,
+                              stream=None):
+    """Paged decode over FP8 E4M3 pools [num_blocks,H_kv,block_size,d] (uint8 codes)."""
+    lib = load()
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, dev)
+    k_pool = _codes("k_pool", k_pool, dev)
+    v_pool = _codes("v_pool", v_pool, dev)
+    _check_tensor("block_table", block_table, torch.int32, dev, ndim=2)
+    B, H_q, N_q, d = q.shape
+    num_blocks, H_kv, block_size, _ = k_pool.shape
+    if tuple(k_pool.shape) != (num_blocks, H_kv, block_size, d) or v_pool.shape != k_pool.shape:
+        raise ValueError("pool shapes do not match q")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have B rows")
+    max_blocks = block_table.shape[1]
+    if kv_lens is not None:
+        _check_tensor("kv_lens", kv_lens, torch.int32, dev, ndim=1)
+        if kv_lens.shape[0] != B:
+            raise ValueError("kv_lens must have B entries")
+    if o is None:
+        o = torch.empty_like(q)
+    _check_tensor("o", o, q.dtype, dev)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, dev, ndim=3)
+    need = attn_decode_paged_workspace_size(B, H_q, H_kv, N_q, max_blocks, block_size, d, ATTN_BF16)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(dev):
+        st = lib.attn_decode_paged_fp8_fwd(_ptr(q), _ptr(k_pool), _ptr(v_pool), float(k_scale),
+                                           float(v_scale), _ptr(block_table), _ptr(kv_lens), _ptr(o),
+                                           _ptr(lse), B, H_q, H_kv, N_q, max_blocks, block_size,
+                                           num_blocks, d, int(bool(causal)), float(scale), ATTN_BF16,
+                                           _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream(dev, stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_paged_fp8_fwd")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
 __all__ = ["attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_size",
-           "attn_decode_paged_fwd", "attn_decode_paged_workspace_size", "attn_status_string",
+           "attn_decode_paged_fwd", "attn_decode_paged_workspace_size", "attn_decode_fp8_fwd",
+           "attn_decode_paged_fp8_fwd", "attn_status_string",
            "attn_version", "load", "AttnError", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

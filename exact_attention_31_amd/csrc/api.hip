@@ -136,12 +136,18 @@ int log2_of(int v) {
 int decode_launch(const void* q, const void* k, const void* v, size_t kv_bytes, const int* table,
                   int max_blocks, int block_size, int num_blocks, const int* kv_lens, void* o,
                   float* lse, int B, int H_q, int H_kv, int N_q, int N_kv, int d, int causal,
-                  float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                  float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                  bool kv_fp8 = false, float k_scale = 1.f, float v_scale = 1.f) {
   const bool paged = table != nullptr || block_size != 0;
   int st = check_common(B, H_q, H_kv, N_q, N_kv, d, dtype, scale);
   if (st != ATTN_OK) return st;
   if (causal != 0 && causal != 1) return ATTN_ERR_VALUE;
   if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (kv_fp8) {
+    if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(k_scale) || !(k_scale > 0.f) || !isfinite(v_scale) || !(v_scale > 0.f))
+      return ATTN_ERR_VALUE;
+  }
   if (N_q > attn::kDecodeMaxNq) return ATTN_ERR_UNSUPPORTED;
   if (B == 0 || H_q == 0 || N_q == 0) return ATTN_OK;
   if (q == nullptr || o == nullptr) return ATTN_ERR_NULL;
@@ -158,7 +164,8 @@ int decode_launch(const void* q, const void* k, const void* v, size_t kv_bytes, 
       (int64_t)B * H_kv * groups * plan.splits > 0x3fffffffLL)
     return ATTN_ERR_SHAPE;
   // contiguous caches: per-head byte offsets are 32-bit (buffer addressing)
-  if (!paged && (int64_t)N_kv * d * elem_size(dtype) > 0xffffffffLL) return ATTN_ERR_SHAPE;
+  if (!paged && (int64_t)N_kv * d * (kv_fp8 ? 1 : elem_size(dtype)) > 0xffffffffLL)
+    return ATTN_ERR_SHAPE;
   if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE;
   const size_t es = elem_size(dtype);
   const size_t nq = (size_t)B * H_q * N_q * d * es;
@@ -185,7 +192,7 @@ int decode_launch(const void* q, const void* k, const void* v, size_t kv_bytes, 
                      plan.chunk, plan.splits, g_dev_cus[dev], ws,
                      ws + (size_t)B * H_q * N_q * plan.splits * d,
                      paged ? table : nullptr, max_blocks, paged ? log2_of(block_size) : 0,
-                     num_blocks};
+                     num_blocks, kv_fp8 ? 1 : 0, k_scale, v_scale};
   return attn::launch_decode(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -232,6 +239,32 @@ int attn_decode_paged_fwd(const void* q, const void* k_pool, const void* v_pool,
   return decode_launch(q, k_pool, v_pool, npool, block_table, max_blocks, block_size, num_blocks,
                        kv_lens, o, lse, B, H_q, H_kv, N_q, (int)n, d, causal, scale, dtype,
                        workspace, workspace_bytes, stream);
+}
+
+int attn_decode_fp8_fwd(const void* q, const void* k_cache, const void* v_cache, float k_scale,
+                        float v_scale, const int* kv_lens, void* o, float* lse, int B, int H_q,
+                        int H_kv, int N_q, int N_kv, int d, int causal, float scale, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  const size_t nkv = (B > 0 && H_kv > 0 && N_kv > 0 && d > 0) ? (size_t)B * H_kv * N_kv * d : 0;
+  return decode_launch(q, k_cache, v_cache, nkv, nullptr, 0, 0, 0, kv_lens, o, lse, B, H_q, H_kv,
+                       N_q, N_kv, d, causal, scale, dtype, workspace, workspace_bytes, stream, true,
+                       k_scale, v_scale);
+}
+
+int attn_decode_paged_fp8_fwd(const void* q, const void* k_pool, const void* v_pool,
+                              float k_scale, float v_scale, const int* block_table,
+                              const int* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
+                              int N_q, int max_blocks, int block_size, int num_blocks, int d,
+                              int causal, float scale, int dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const int64_t n = paged_capacity(max_blocks, block_size, num_blocks);
+  if (n == -2) return ATTN_ERR_UNSUPPORTED;
+  if (n < 0) return ATTN_ERR_SHAPE;
+  const size_t npool =
+      (num_blocks > 0 && H_kv > 0 && d > 0) ? (size_t)num_blocks * H_kv * block_size * d : 0;
+  return decode_launch(q, k_pool, v_pool, npool, block_table, max_blocks, block_size, num_blocks,
+                       kv_lens, o, lse, B, H_q, H_kv, N_q, (int)n, d, causal, scale, dtype,
+                       workspace, workspace_bytes, stream, true, k_scale, v_scale);
 }
 
 }  // extern "C"

@@ -45,6 +45,9 @@ struct DecodeArgs {
   int max_blocks;
   int block_size_log2;
   int num_blocks;
+  // FP8 E4M3 caches (kv_fp8 != 0): one byte per element, value = code * scale
+  int kv_fp8;
+  float k_scale, v_scale;
 };
 
 // Split plan shared by the workspace query and the launch.

@@ -50,10 +50,11 @@ template <int D> struct DecLds {
 // [B, H_kv, N_kv, d]. Paged caches are a pool of fixed-size blocks
 // [num_blocks, H_kv, block_size, d] plus a per-request block table
 // [B, max_blocks] that maps logical block i (positions i*block_size ..
-// (i+1)*block_size - 1) to a physical block of the pool.
+// (i+1)*block_size - 1) to a physical block of the pool. Elements are 16-bit
+// (the query's type) or FP8 E4M3 codes.
 struct KvSrc {
-  const uint16_t* k;
-  const uint16_t* v;
+  const uint8_t* k;
+  const uint8_t* v;
   const int* table;     // paged only
   int max_blocks;       // paged only: table row length
   int bs_log2;          // paged only: log2(block_size), block_size >= 16
@@ -67,22 +68,36 @@ struct SplitParams {
   float* part_u;
   float* part_ml;
   int B, H_q, H_kv, N_q, N_kv, causal, splits, chunk;
-  float scale_log2;
+  float scale_log2;  // softmax scale * log2(e) (times the K dequantisation scale for FP8)
 };
+
+// Four FP8 E4M3 codes (one dword) to four bf16 values (two dwords), exactly:
+// every E4M3 value is a bf16 value.
+__device__ __forceinline__ u32x2_t fp8x4_to_bf16(uint32_t w) {
+  const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
 
 // One work unit, done by one wavefront alone: keys [split*chunk,
 // min((split+1)*chunk, len)) of request b for KV head hk and query column
 // groups NG*qg .. NG*qg + NG-1 (16 columns each). Writes that chunk's partial
 // (u, m, l) for the groups' query rows. The NG groups share every K register
 // and every V operand read from LDS; only the matrix products are per group.
-template <class TT, int D, int NG, bool PAGED>
+// FP8: K and V are E4M3 codes, widened to bf16 in registers (K) or on their way
+// into LDS (V); the dequantisation scales are applied to the score scale and,
+// in the merge, to the output.
+template <class TT, int D, int NG, bool PAGED, bool FP8>
 __device__ __forceinline__ void wave_unit(const SplitParams& P, int b, int hk, int qg, int split,
                                           int len, uint16_t* sV) {
   constexpr int VST = DecLds<D>::VST;
   constexpr int KS = D / 32;        // k-steps of the score MFMA
   constexpr int DB = D / 16;        // 16-wide output blocks
-  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int EB = FP8 ? 1 : 2;   // bytes per cached element
+  constexpr int RB = D * EB;        // bytes per cached row
+  constexpr int CPR = RB / 16;      // 16-byte chunks per cached row
   constexpr int VL = kWaveKeys * CPR / 64;  // V loads per lane per step (half per 16 rows)
+  constexpr int KL = FP8 ? D / 64 : KS;     // K loads per lane per 16 keys
 
   const int lane = threadIdx.x & 63;
   const int c16 = lane & 15;   // query column (S^T) / output row
@@ -97,12 +112,12 @@ __device__ __forceinline__ void wave_unit(const SplitParams& P, int b, int hk, i
   // ---- cache addressing. rows16(r0) is a buffer resource over rows r0 ..
   // r0 + 15 of this request and KV head (r0 a multiple of 16) bounded by the
   // request's length: rows past it read as zeros.
-  const uint16_t* Kh = nullptr;
-  const uint16_t* Vh = nullptr;
+  const uint8_t* Kh = nullptr;
+  const uint8_t* Vh = nullptr;
   int tb0 = -1, tb1 = -1, blk0 = 0;
   if constexpr (!PAGED) {
-    Kh = P.kv.k + ((int64_t)b * H_kv + hk) * (int64_t)P.N_kv * D;
-    Vh = P.kv.v + ((int64_t)b * H_kv + hk) * (int64_t)P.N_kv * D;
+    Kh = P.kv.k + ((int64_t)b * H_kv + hk) * (int64_t)P.N_kv * RB;
+    Vh = P.kv.v + ((int64_t)b * H_kv + hk) * (int64_t)P.N_kv * RB;
   } else {
     // this chunk's block-table entries, one per lane (a chunk spans at most
     // 128 blocks); entries of blocks past the request's length are not read
@@ -113,10 +128,10 @@ __device__ __forceinline__ void wave_unit(const SplitParams& P, int b, int hk, i
     if (blk0 + lane < nblk) tb0 = trow[blk0 + lane];
     if (blk0 + 64 + lane < nblk) tb1 = trow[blk0 + 64 + lane];
   }
-  auto rows16 = [&](const uint16_t* base, int r0) {
+  auto rows16 = [&](const uint8_t* base, int r0) {
     if constexpr (!PAGED) {
       const int n = max(0, len - r0);
-      return buffer_rsrc(base + (int64_t)min(r0, len) * D, (uint32_t)n * D * 2);
+      return buffer_rsrc(base + (int64_t)min(r0, len) * RB, (uint32_t)n * RB);
     } else {
       const int bsl = P.kv.bs_log2;
       const int li = (r0 >> bsl) - blk0;   // wavefront-uniform
@@ -126,11 +141,11 @@ __device__ __forceinline__ void wave_unit(const SplitParams& P, int b, int hk, i
       const bool ok = (unsigned)pb < (unsigned)P.kv.num_blocks && r0 < len;
       const int n = ok ? min((1 << bsl) - off, len - r0) : 0;
       const int64_t row = ok ? (((int64_t)pb * H_kv + hk) << bsl) + off : 0;
-      return buffer_rsrc(base + row * D, (uint32_t)n * D * 2);
+      return buffer_rsrc(base + row * RB, (uint32_t)n * RB);
     }
   };
-  const uint16_t* kbase = PAGED ? P.kv.k : Kh;
-  const uint16_t* vbase = PAGED ? P.kv.v : Vh;
+  const uint8_t* kbase = PAGED ? P.kv.k : Kh;
+  const uint8_t* vbase = PAGED ? P.kv.v : Vh;
 
   // The G query heads of KV head hk, N_q query rows each, are G*N_q contiguous
   // rows of Q; they are the MFMA's query columns, 16 per group.
@@ -146,15 +161,20 @@ __device__ __forceinline__ void wave_unit(const SplitParams& P, int b, int hk, i
     lim[j] = P.causal ? min(len, len - N_q + qi + 1) : len;
   }
 
-  // Q^T operands: column c16 of group j = row col0[j] + c16 of the block,
-  // K-slots d = 32*st + 8*g + 0..7
+  // Which head-dim slots lane group g feeds to k-step st. Any assignment works
+  // if Q and K agree; 16-bit K uses d = 32*st + 8*g + 0..7, FP8 K gives each
+  // lane group one contiguous run of D/4 codes (d = (D/4)*g + 8*st + 0..7) so
+  // that its bytes come in whole 16-byte loads.
+  auto dslot = [&](int st) { return FP8 ? (D / 4) * g + 8 * st : 32 * st + 8 * g; };
+
+  // Q^T operands: column c16 of group j = row col0[j] + c16 of the block
   u32x4_t qreg[NG][KS];
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
     const auto rQ = buffer_rsrc(P.q + (qrow0 + min(col0[j], G * N_q)) * D, (uint32_t)ncols[j] * D * 2);
 #pragma unroll
     for (int st = 0; st < KS; ++st)
-      qreg[j][st] = buffer_load16(rQ, (uint32_t)(c16 * D + 32 * st + 8 * g) * 2);
+      qreg[j][st] = buffer_load16(rQ, (uint32_t)(c16 * D + dslot(st)) * 2);
   }
 
   f32x4_t oacc[NG][DB];
@@ -169,29 +189,55 @@ __device__ __forceinline__ void wave_unit(const SplitParams& P, int b, int hk, i
     l[j] = 0.f;
   }
 
-  // K rows feed the A operand directly: key = w0 + 16*kb + c16, d = 32*st + 8*g.
-  // V rows: lane takes 16-byte chunk c = lane + 64*i of the step's rows (row
-  // c / CPR, column c % CPR); the first VL/2 chunks are rows 0..15. The lane
-  // offsets are fixed; each 16-row half has its own wavefront-uniform resource.
-  const uint32_t koff = (uint32_t)(c16 * D + 8 * g) * 2;
+  // K rows feed the A operand directly: key = w0 + 16*kb + c16. V rows: lane
+  // takes 16-byte chunk c = lane + 64*i of the step's rows (row c / CPR, chunk
+  // c % CPR); the first VL/2 chunks are rows 0..15. The lane offsets are fixed;
+  // each 16-row half has its own wavefront-uniform resource.
+  const uint32_t koff = FP8 ? (uint32_t)(c16 * RB + (D / 4) * g) : (uint32_t)(c16 * D + 8 * g) * 2;
   const uint32_t voff = (uint32_t)lane * 16;
-  u32x4_t ka[2][2][KS], va[2][VL];
-  auto issue = [&](int w0, u32x4_t (&kk)[2][KS], u32x4_t (&vv)[VL]) {
+  u32x4_t ka[2][2][KL], va[2][VL];
+  auto issue = [&](int w0, u32x4_t (&kk)[2][KL], u32x4_t (&vv)[VL]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const auto rK = rows16(kbase, w0 + 16 * h);
       const auto rV = rows16(vbase, w0 + 16 * h);
 #pragma unroll
-      for (int st = 0; st < KS; ++st) kk[h][st] = buffer_load16(rK, koff + 64 * st);
+      for (int st = 0; st < KL; ++st) kk[h][st] = buffer_load16(rK, koff + (FP8 ? 16 : 64) * st);
 #pragma unroll
       for (int i = 0; i < VL / 2; ++i) vv[h * (VL / 2) + i] = buffer_load16(rV, voff + 1024 * i);
     }
   };
-  auto step = [&](int w0, const u32x4_t (&kk)[2][KS], const u32x4_t (&vv)[VL]) {
+  auto step = [&](int w0, const u32x4_t (&kraw)[2][KL], const u32x4_t (&vv)[VL]) {
+    // V rows into LDS as 16-bit values
 #pragma unroll
     for (int i = 0; i < VL; ++i) {
       const int c = lane + 64 * i;
-      *(u32x4_t*)(sV + (c / CPR) * VST + (c % CPR) * 8) = vv[i];
+      if constexpr (FP8) {
+        const u32x2_t a = fp8x4_to_bf16(vv[i][0]), b2 = fp8x4_to_bf16(vv[i][1]);
+        const u32x2_t c2 = fp8x4_to_bf16(vv[i][2]), d2 = fp8x4_to_bf16(vv[i][3]);
+        uint16_t* dst = sV + (c / CPR) * VST + (c % CPR) * 16;
+        *(u32x4_t*)dst = u32x4_t{a[0], a[1], b2[0], b2[1]};
+        *(u32x4_t*)(dst + 8) = u32x4_t{c2[0], c2[1], d2[0], d2[1]};
+      } else {
+        *(u32x4_t*)(sV + (c / CPR) * VST + (c % CPR) * 8) = vv[i];
+      }
+    }
+    // K operands: 16-bit rows as loaded; FP8 codes widened (8 per k-step)
+    u32x4_t kk[2][KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if constexpr (FP8) {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const u32x4_t& w = kraw[kb][st / 2];
+          const u32x2_t x = fp8x4_to_bf16(w[(st & 1) * 2]);
+          const u32x2_t y = fp8x4_to_bf16(w[(st & 1) * 2 + 1]);
+          kk[kb][st] = u32x4_t{x[0], x[1], y[0], y[1]};
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) kk[kb][st] = kraw[kb][st];
+      }
     }
     u32x4_t bop[NG];
 #pragma unroll
@@ -291,7 +337,7 @@ __device__ __forceinline__ void wave_unit(const SplitParams& P, int b, int hk, i
 // handing units out round-robin to the wavefronts of the grid balances ragged
 // lengths without atomics or barriers. Each wavefront walks the requests
 // forward as its unit index grows, reading kv_lens as it goes.
-template <class TT, int D, int NG, int OCC, bool PAGED>
+template <class TT, int D, int NG, int OCC, bool PAGED, bool FP8>
 __global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(const SplitParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[DecLds<D>::kV];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -320,19 +366,20 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(const Split
       }
     }
     if (cb >= B) break;
-    wave_unit<TT, D, NG, PAGED>(P, cb, hg / ngroups, hg - (hg / ngroups) * ngroups, c - cstart, lb, sV);
+    wave_unit<TT, D, NG, PAGED, FP8>(P, cb, hg / ngroups, hg - (hg / ngroups) * ngroups, c - cstart, lb, sV);
   }
 }
 
 // Merge of the split partials: out = sum_s w_s u_s / sum_s w_s l_s with
-// w_s = exp2(m_s - max_s m_s). One 64-lane wavefront per query row
-// (request, query head, query index); lane i owns output column i (d = 64) or
-// columns 2i, 2i+1 (d = 128).
+// w_s = exp2(m_s - max_s m_s), times out_scale (the V dequantisation scale
+// of an FP8 cache, else 1). One 64-lane wavefront per query row (request,
+// query head, query index); lane i owns output column i (d = 64) or columns
+// 2i, 2i+1 (d = 128).
 template <class TT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part_u, const float* __restrict__ part_ml,
     const int* __restrict__ kv_lens, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int rows_per_b, int N_kv, int splits, int chunk, int BH) {
+    int rows_per_b, int N_kv, int splits, int chunk, int BH, float out_scale) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int PER = D / 64;  // columns per lane
   const int lane = threadIdx.x & 63;
@@ -380,7 +427,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+  const float inv = (L > 0.f) ? out_scale / L : 0.f;
   uint16_t* out = O + (int64_t)bh * D + PER * lane;
   if constexpr (PER == 2) {
     *(uint32_t*)out = TT::pack2(U0 * inv, U1 * inv);
@@ -390,7 +437,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   if (LSE != nullptr && lane == 0) LSE[bh] = (L > 0.f) ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
-template <class TT, int D, int NG, int OCC>
+template <class TT, int D, int NG, int OCC, bool FP8>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   const int G = a.H_q / a.H_kv;
   const int ngroups = (G * a.N_q + NG * kQCols - 1) / (NG * kQCols);
@@ -401,7 +448,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(wgs < slots ? wgs : slots));
   SplitParams P;
   P.q = (const uint16_t*)a.q;
-  P.kv = KvSrc{(const uint16_t*)a.k, (const uint16_t*)a.v, a.block_table, a.max_blocks,
+  P.kv = KvSrc{(const uint8_t*)a.k, (const uint8_t*)a.v, a.block_table, a.max_blocks,
                a.block_size_log2, a.num_blocks};
   P.kv_lens = a.kv_lens;
   P.part_u = a.part_u;
@@ -414,21 +461,21 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   P.causal = a.causal;
   P.splits = a.splits;
   P.chunk = a.chunk;
-  P.scale_log2 = a.scale * kLog2e;
+  P.scale_log2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
   if (a.block_table != nullptr)
-    hipLaunchKernelGGL((decode_split_kernel<TT, D, NG, OCC, true>), grid, dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL((decode_split_kernel<TT, D, NG, OCC, true, FP8>), grid, dim3(kThreads), 0, st, P);
   else
-    hipLaunchKernelGGL((decode_split_kernel<TT, D, NG, OCC, false>), grid, dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL((decode_split_kernel<TT, D, NG, OCC, false, FP8>), grid, dim3(kThreads), 0, st, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int BH = a.B * a.H_q * a.N_q;
   hipLaunchKernelGGL((decode_merge_kernel<TT, D>), dim3((BH + 3) / 4), dim3(256), 0, st, a.part_u,
                      a.part_ml, a.kv_lens, (uint16_t*)a.o, a.lse, a.H_q * a.N_q, a.N_kv, a.splits,
-                     a.chunk, BH);
+                     a.chunk, BH, FP8 ? a.v_scale : 1.f);
   return hipGetLastError();
 }
 
-template <class TT>
+template <class TT, bool FP8>
 hipError_t launch_dtype(const DecodeArgs& a, hipStream_t st) {
   // more than 16 query rows per KV head: each wavefront serves two or four
   // column groups, so K and V are read once per 32 or 64 rows
@@ -440,11 +487,11 @@ hipError_t launch_dtype(const DecodeArgs& a, hipStream_t st) {
     if (f == 1 || f == 2 || f == 4) ng = f;
   }
   if (a.d == 64) {
-    if (ng == 1) return launch_t<TT, 64, 1, 2>(a, st);
-    return ng == 2 ? launch_t<TT, 64, 2, 2>(a, st) : launch_t<TT, 64, 4, 2>(a, st);
+    if (ng == 1) return launch_t<TT, 64, 1, 2, FP8>(a, st);
+    return ng == 2 ? launch_t<TT, 64, 2, 2, FP8>(a, st) : launch_t<TT, 64, 4, 2, FP8>(a, st);
   }
-  if (ng == 1) return launch_t<TT, 128, 1, 2>(a, st);
-  return ng == 2 ? launch_t<TT, 128, 2, 1>(a, st) : launch_t<TT, 128, 4, 1>(a, st);
+  if (ng == 1) return launch_t<TT, 128, 1, 2, FP8>(a, st);
+  return ng == 2 ? launch_t<TT, 128, 2, 1, FP8>(a, st) : launch_t<TT, 128, 4, 1, FP8>(a, st);
 }
 
 }  // namespace
@@ -474,8 +521,10 @@ DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool 
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  if (a.dtype == kDtypeBF16) return launch_dtype<BF16>(a, st);
-  return launch_dtype<F16>(a, st);
+  // FP8 caches are widened to bf16, so they pair with bf16 queries only
+  if (a.kv_fp8) return launch_dtype<BF16, true>(a, st);
+  if (a.dtype == kDtypeBF16) return launch_dtype<BF16, false>(a, st);
+  return launch_dtype<F16, false>(a, st);
 }
 
 }  // namespace attn

@@ -137,6 +137,43 @@ int attn_decode_paged_fwd(const void* q, const void* k_pool, const void* v_pool,
                           int num_blocks, int d, int causal, float scale, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode forward over an FP8 KV cache: keys and values are stored as OCP FP8
+ * E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, 0x7F/0xFF NaN) with one dequantisation scale per tensor: the
+ * cached value is code_value * k_scale (keys) or * v_scale (values). This halves
+ * the bytes decode reads against 16-bit caches; the pages measure decode with
+ * an FP8 KV cache (code-journey.com attention co-design summary, arithmetic
+ * intensity formulas and decode measurements).
+ * Codes are widened exactly to bf16 inside the kernel (every E4M3 value is a
+ * bf16 value), so the result is attention over the dequantised cache, computed
+ * as for a bf16 cache. Same layout and semantics as attn_decode_fwd with K/V
+ * elements of one byte:
+ *   k_cache/v_cache [B,H_kv,N_kv,d] uint8 E4M3 codes; q, o bf16 (dtype must be
+ *   ATTN_BF16, else ATTN_ERR_UNSUPPORTED);
+ *   k_scale, v_scale: positive and finite (else ATTN_ERR_VALUE);
+ *   workspace: attn_decode_workspace_size(B, H_q, H_kv, N_q, N_kv, d, ATTN_BF16)
+ *   bytes.
+ * Work: 2 * kv_lens[b] * H_kv * d bytes of K and V read.
+ */
+int attn_decode_fp8_fwd(const void* q, const void* k_cache, const void* v_cache, float k_scale,
+                        float v_scale, const int* kv_lens, void* o, float* lse, int B, int H_q,
+                        int H_kv, int N_q, int N_kv, int d, int causal, float scale, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Paged FP8 decode: attn_decode_paged_fwd over pools of E4M3 codes
+ * [num_blocks, H_kv, block_size, d] (uint8) with per-tensor scales as in
+ * attn_decode_fp8_fwd. Workspace: attn_decode_paged_workspace_size(...,
+ * ATTN_BF16) bytes.
+ */
+int attn_decode_paged_fp8_fwd(const void* q, const void* k_pool, const void* v_pool,
+                              float k_scale, float v_scale, const int* block_table,
+                              const int* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
+                              int N_q, int max_blocks, int block_size, int num_blocks, int d,
+                              int causal, float scale, int dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_string(int status);
 

@@ -3,5 +3,5 @@ the tests, the smoke check and the benchmark's CPU-baseline leg, never by the
 HIP library or its Python binding."""
 from .attention import (  # noqa: F401
     MiB, attention_flops, kv_cache_bytes, attention_head_rows, attention_ref, score_bytes, softmax_weights,
-    visible_pairs, gather_paged, attention_paged_ref,
+    visible_pairs, gather_paged, attention_paged_ref, e4m3_value, dequant_e4m3, attention_fp8kv_ref,
 )

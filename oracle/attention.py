@@ -36,6 +36,12 @@ What it computes (the plain definition, written out):
   "Block-wise KV Cache" in its recent-trends and method sections). Attention
   over it is attention over the cache that the block table describes: gather
   the blocks into a contiguous cache, then apply the definition above.
+* An FP8 KV cache (the pages' decode measurements assume one: code-journey.com
+  attention co-design summary, arithmetic-intensity formulas) holds E4M3 codes
+  and a per-tensor scale; attention over it is attention over the dequantised
+  values code_value * scale. E4M3 here is the OCP 8-bit format: 1 sign bit,
+  4 exponent bits (bias 7), 3 mantissa bits, subnormals at exponent 0, no
+  infinities, and S.1111.111 the only NaN pattern.
 
 All arithmetic is float64 on the exact (dtype-rounded) input values; numpy's
 matmul (BLAS dgemm) forms the score rows and the weighted sum.
@@ -187,6 +193,34 @@ def attention_paged_ref(q, k_pool, v_pool, block_table, kv_lens, block_size: int
     return attention_ref(q, k, v, causal, scale, kv_lens=kv_lens)
 
 
+def e4m3_value(code: int) -> float:
+    """The value of one OCP FP8 E4M3 code, from the bit fields."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return float("nan")
+    if exp == 0:                      # subnormal: 0.man * 2^(1 - bias)
+        return sign * (man / 8.0) * 2.0 ** (1 - 7)
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def dequant_e4m3(codes, scale: float) -> np.ndarray:
+    """float64 values code_value * scale of an array of E4M3 codes (uint8)."""
+    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)] * float(scale)
+
+
+def attention_fp8kv_ref(q, k_codes, v_codes, k_scale: float, v_scale: float, causal: bool,
+                        scale: float, kv_lens=None):
+    """Exact attention over an FP8 cache: attention_ref on the dequantised K and V."""
+    return attention_ref(q, dequant_e4m3(k_codes, k_scale), dequant_e4m3(v_codes, v_scale), causal,
+                         scale, kv_lens=kv_lens)
+
+
 def softmax_weights(scores: np.ndarray) -> np.ndarray:
     """Row softmax of a score matrix (-inf entries get weight 0), float64, two-pass."""
     s = np.asarray(scores, dtype=np.float64)
@@ -202,5 +236,5 @@ def attention_flops(N_q: int, n: int, d: int, causal: bool) -> int:
 
 
 __all__ = ["score_bytes", "kv_cache_bytes", "visible_pairs", "attention_ref", "attention_head_rows",
-           "gather_paged", "attention_paged_ref",
+           "gather_paged", "attention_paged_ref", "e4m3_value", "dequant_e4m3", "attention_fp8kv_ref",
            "softmax_weights", "attention_flops", "MiB"]

@@ -137,3 +137,22 @@ def test_paged_decode_argument_errors():
     assert pdf(table=FAKE[3]) == 8   # block table overlaps the output
     assert pdf(B=0) == 0
     assert pdf() == 7 and pdf(bs=4096, maxb=3) == 7 and pdf(nblk=0) == 7
+
+
+def f8(scale_k=0.02, scale_v=0.03, dtype=E.ATTN_BF16, Nq=1, ws=P(0x7000000000), wsb=None, **kw):
+    a = dict(B=2, Hq=8, Hkv=1, Nkv=1000, d=128)
+    a.update(kw)
+    if wsb is None:
+        wsb = ws_size(a["B"], a["Hq"], a["Hkv"], Nq, a["Nkv"], a["d"], E.ATTN_BF16)
+    return L.attn_decode_fp8_fwd(FAKE[0], FAKE[1], FAKE[2], scale_k, scale_v, None, FAKE[3], None,
+                                 a["B"], a["Hq"], a["Hkv"], Nq, a["Nkv"], a["d"], 0, 0.088, dtype,
+                                 ws, wsb, None)
+
+
+def test_fp8_decode_argument_errors():
+    assert f8(dtype=E.ATTN_F16) == 4 and f8(dtype=E.ATTN_F32) == 4 and f8(d=96) == 4
+    assert f8(scale_k=0.0) == 9 and f8(scale_v=-1.0) == 9 and f8(scale_k=float("inf")) == 9
+    assert f8(ws=None) == 5
+    assert f8(Hq=12, Hkv=8) == 3
+    assert f8(B=0) == 0
+    assert f8() == 7 and f8(Nq=5) == 7
