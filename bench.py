@@ -13,6 +13,7 @@ Default run (one JSON line on stdout):
     (causal, bottom-right aligned), as a speculative-decoding verifier sees it;
   * "decode_paged" times the same caches cut into 16-position blocks scattered
     over a pool and read through a block table;
+  * "decode_fp8" times the same caches stored as FP8 E4M3 codes (half the bytes);
   * "cpu_baseline" times the float64 oracle on a bounded sample of the prefill
     workload on this host's cores.
 `--all` also times the other three workloads (fp32 single head, the 23,400-step
@@ -194,6 +195,34 @@ def bench_decode_paged(cfg, steps, warmup, torch, E, cache, block_size=16):
             "peak_gb_per_s": PEAK_HBM, "wall_s": wall, "equals_contiguous": same}
 
 
+def bench_decode_fp8(cfg, steps, warmup, torch, E, cache, k_scale=2.0 ** -6, v_scale=2.0 ** -6):
+    """Decode over an FP8 E4M3 copy of `cache` (codes = E4M3(value / scale),
+    per-tensor scales); bytes counted are the FP8 bytes read."""
+    import attn_inputs as A
+    k, v = cache
+    B, H_kv, N, d = k.shape
+    kc = (k.float() / k_scale).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    vc = (v.float() / v_scale).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    lens = np.full(B, N, np.int32)
+    q = make_device_tensor(cfg, "q", torch)
+    o = torch.empty_like(q)
+    lens_d = torch.from_numpy(lens).cuda()
+    ws = torch.empty(E.attn_decode_workspace_size(B, cfg.H_q, H_kv, cfg.N_q, N, d, q.dtype),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        E.attn_decode_fp8_fwd(q, kc, vc, k_scale, v_scale, o, kv_lens=lens_d, scale=cfg.scale,
+                              causal=cfg.causal, workspace=ws)
+
+    ms, wall = time_launches(call, steps, warmup, torch)
+    nbytes = decode_kv_bytes(cfg, lens) // 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del kc, vc, q, o, ws
+    return {"config": f"{cfg.cid}-fp8", "name": cfg.name + ", FP8 E4M3 cache", "ms": ms,
+            "kv_bytes": nbytes, "gb_per_s": gbs, "frac_of_peak": gbs / PEAK_HBM,
+            "peak_gb_per_s": PEAK_HBM, "wall_s": wall}
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=3):
     """A plain device-to-device copy of known size (torch's copy kernel): the
     HBM counters read for it calibrate the FETCH_SIZE / WRITE_SIZE scale."""
@@ -266,7 +295,7 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="also time configs 1, 3, 4 and ragged decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["prefill", "decode", "decode_ragged", "decode_multi",
-                                       "decode_paged"], default=None)
+                                       "decode_paged", "decode_fp8"], default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for HBM counter calibration)")
@@ -313,6 +342,15 @@ def main(argv=None):
               f"same bits as contiguous: {r['equals_contiguous']}", file=sys.stderr, flush=True)
         res["decode_paged"] = r
         if args.only == "decode_paged":
+            res["decode"] = r
+    if args.only in (None, "decode_fp8"):
+        if cache is None:
+            _, cache = bench_decode(A.CONFIGS[5], 1, 1, torch, E)
+        r = bench_decode_fp8(A.CONFIGS[5], args.steps, args.warmup, torch, E, cache)
+        print(f"# decode c5 FP8 cache: {r['ms']:.3f} ms  {r['gb_per_s']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        res["decode_fp8"] = r
+        if args.only == "decode_fp8":
             res["decode"] = r
     extra = []
     if args.only == "decode_ragged":
@@ -383,6 +421,14 @@ def main(argv=None):
             "frac_of_hbm_peak": round(dp["frac_of_peak"], 4),
             "equals_contiguous": dp["equals_contiguous"],
             "kernel": "decode_split_kernel<paged> + decode_merge_kernel (one step)"}
+    df8 = res.get("decode_fp8")
+    if df8 and df8 is not d:
+        line["decode_fp8"] = {
+            "workload": "GQA decode over an FP8 E4M3 cache (per-tensor scales), bf16 queries and "
+                        "output, B=64, H_q=32, H_kv=4, d=128, KV 32768 per request",
+            "ms_per_step": round(df8["ms"], 5), "value": round(df8["gb_per_s"], 2), "unit": "GB/s",
+            "frac_of_hbm_peak": round(df8["frac_of_peak"], 4),
+            "kernel": "decode_split_kernel<fp8> + decode_merge_kernel (one step)"}
     if p:
         line["prefill_first_call_ms"] = round(p["first_call_ms"], 3)
     if cpu:
