@@ -60,6 +60,11 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_paged_fp8_fwd.argtypes = [vp, vp, vp, f, f, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                               i, f, i, vp, sz, vp]
     lib.attn_decode_paged_fp8_fwd.restype = i
+    lib.attn_backward_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.attn_backward_workspace_size.restype = sz
+    lib.attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz,
+                                  vp]
+    lib.attn_backward.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -344,7 +349,54 @@ def attn_decode_paged_fp8_fwd(q, k_pool, v_pool, k_scale: float, v_scale: float,
     return (o, lse) if (return_lse or lse is not None) else o
 
 
+def attn_backward_workspace_size(B, H_q, H_kv, N_q, N_kv, d, dtype) -> int:
+    code = DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load().attn_backward_workspace_size(B, H_q, H_kv, N_q, N_kv, d, code))
+
+
+def attn_backward(q, k, v, o, d_o, lse, dq=None, dk=None, dv=None, *, causal: bool = False,
+                  scale: float | None = None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of attention given the forward's o and lse (float32
+    [B,H_q,N_q], natural log) and the output gradient d_o."""
+    lib = load()
+    if q.dtype not in DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("d_o", d_o)):
+        _check_tensor(name, t, q.dtype, dev)
+    _check_tensor("lse", lse, torch.float32, dev, ndim=3)
+    B, H_q, N_q, d = q.shape
+    _, H_kv, N_kv, _ = k.shape
+    if tuple(k.shape) != (B, H_kv, N_kv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k/v shapes do not match q")
+    if tuple(o.shape) != tuple(q.shape) or tuple(d_o.shape) != tuple(q.shape):
+        raise ValueError("o and d_o must have q's shape")
+    if tuple(lse.shape) != (B, H_q, N_q):
+        raise ValueError("lse must be [B, H_q, N_q]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_tensor("dq", dq, q.dtype, dev)
+    _check_tensor("dk", dk, q.dtype, dev)
+    _check_tensor("dv", dv, q.dtype, dev)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("gradient shapes do not match their inputs")
+    need = attn_backward_workspace_size(B, H_q, H_kv, N_q, N_kv, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(dev):
+        st = lib.attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq),
+                               _ptr(dk), _ptr(dv), B, H_q, H_kv, N_q, N_kv, d, int(bool(causal)),
+                               float(scale), DTYPE_CODE[q.dtype], _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    if st != 0:
+        raise AttnError(st, "attn_backward")
+    return dq, dk, dv
+
+
 __all__ = ["attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_size",
            "attn_decode_paged_fwd", "attn_decode_paged_workspace_size", "attn_decode_fp8_fwd",
-           "attn_decode_paged_fp8_fwd", "attn_status_string",
+           "attn_decode_paged_fp8_fwd", "attn_backward", "attn_backward_workspace_size", "attn_status_string",
            "attn_version", "load", "AttnError", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

@@ -7,7 +7,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "prefill.hip", "decode.hip"]
+SOURCES = ["api.hip", "prefill.hip", "decode.hip", "backward.hip"]
 LIB = os.path.join(HERE, "libattn.so")
 
 # Packed fp32 VALU forms are kept out of the generated code.

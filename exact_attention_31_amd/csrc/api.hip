@@ -267,4 +267,52 @@ int attn_decode_paged_fp8_fwd(const void* q, const void* k_pool, const void* v_p
                        workspace, workspace_bytes, stream, true, k_scale, v_scale);
 }
 
+size_t attn_backward_workspace_size(int B, int H_q, int H_kv, int N_q, int N_kv, int d, int dtype) {
+  if (check_common(B, H_q, H_kv, N_q, N_kv, d, dtype, 1.f) != ATTN_OK) return 0;
+  return (size_t)2 * B * H_q * N_q * sizeof(float);
+}
+
+int attn_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int H_q, int H_kv,
+                  int N_q, int N_kv, int d, int causal, float scale, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int st = check_common(B, H_q, H_kv, N_q, N_kv, d, dtype, scale);
+  if (st != ATTN_OK) return st;
+  if (causal != 0 && causal != 1) return ATTN_ERR_VALUE;
+  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  // 1-D grids of 128-row / 128-key blocks; per-head byte offsets are 32-bit
+  if ((int64_t)((N_q + 127) / 128) * H_q * B > 0x7ffffff0LL ||
+      (int64_t)((N_kv + 127) / 128) * H_kv * B > 0x7ffffff0LL)
+    return ATTN_ERR_SHAPE;
+  if ((int64_t)N_q * d * 2 > 0xffffffffLL || (int64_t)N_kv * d * 2 > 0xffffffffLL)
+    return ATTN_ERR_SHAPE;
+  if (B == 0 || H_q == 0 || (N_q == 0 && N_kv == 0)) return ATTN_OK;
+  if (N_q > 0 && (q == nullptr || o == nullptr || d_o == nullptr || lse == nullptr || dq == nullptr))
+    return ATTN_ERR_NULL;
+  if (N_kv > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return ATTN_ERR_NULL;
+  const size_t need = (size_t)2 * B * H_q * N_q * sizeof(float);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * H_q * N_q * d * es;
+  const size_t nkv = (size_t)B * H_kv * N_kv * d * es;
+  const size_t nl = (size_t)B * H_q * N_q * sizeof(float);
+  const void* ins[6] = {q, k, v, o, d_o, lse};
+  const size_t in_sz[6] = {nq, nkv, nkv, nq, nq, nl};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const size_t out_sz[4] = {nq, nkv, nkv, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return ATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return ATTN_ERR_ALIAS;
+  }
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  float* ws = (float*)workspace;
+  attn::BackwardArgs a{q, k, v, o, d_o, lse, dq, dk, dv, B, H_q, H_kv, N_q, N_kv, d, causal,
+                       scale, dtype, ws, ws + (size_t)B * H_q * N_q};
+  return attn::launch_backward(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 }  // extern "C"

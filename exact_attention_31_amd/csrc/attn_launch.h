@@ -59,7 +59,26 @@ struct DecodePlan {
 DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool paged);
 constexpr int kDecodeMaxNq = 64;  // query tokens per request the decode path takes
 
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* d_o;
+  const float* lse;  // [B, H_q, N_q] natural log, from the forward pass
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H_q, H_kv, N_q, N_kv, d;
+  int causal;
+  float scale;
+  int dtype;
+  float* lse2;   // workspace [B, H_q, N_q]: lse in log2 units (+inf for empty rows)
+  float* delta;  // workspace [B, H_q, N_q]: rowsum(dO * O)
+};
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace attn

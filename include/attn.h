@@ -174,6 +174,39 @@ int attn_decode_paged_fp8_fwd(const void* q, const void* k_pool, const void* v_p
                               int causal, float scale, int dtype, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of device workspace attn_backward needs: 2 * B * H_q * N_q floats (0 if
+ * the sizes are invalid).
+ */
+size_t attn_backward_workspace_size(int B, int H_q, int H_kv, int N_q, int N_kv, int d, int dtype);
+
+/*
+ * Backward pass by recomputation: the forward pass keeps only O and the per-row
+ * log-sum-exp; this call rebuilds the probability tiles from Q, K and that
+ * statistic instead of reading a stored score matrix (marketmaker.cc,
+ * "Rückwärtsdurchlauf: Neu berechnen statt speichern"). With S = scale Q K^T,
+ * P = exp(S - lse) (masked entries 0) and Delta_i = sum_d dO_id O_id:
+ *   dV = P^T dO,  dS = P o (dO V^T - Delta),  dQ = scale dS K,  dK = scale dS^T Q,
+ * dK and dV summed over the H_q / H_kv query heads of each KV head.
+ *   q, o, d_o, dq [B,H_q,N_q,d]; k, v, dk, dv [B,H_kv,N_kv,d]; all of `dtype`
+ *   (ATTN_BF16 or ATTN_F16; ATTN_F32 is ATTN_ERR_UNSUPPORTED);
+ *   lse: float32 [B,H_q,N_q], the natural-log LSE that attn_prefill_fwd returned
+ *   for the same q, k, v, causal and scale (o likewise its output);
+ *   causal, scale: as for attn_prefill_fwd (bottom-right alignment);
+ *   workspace: attn_backward_workspace_size(...) bytes, overwritten.
+ * dq, dk, dv are written in full (no accumulation into them); they must not
+ * overlap any input, each other or the workspace. Three kernels run on
+ * `stream`: per-row Delta, then dK/dV (one workgroup per 128 keys), then dQ
+ * (one workgroup per 128 query rows); no atomics, so results are
+ * deterministic.
+ * Work: 10*d FLOP per visible (query, key) pair per query head in the five
+ * products (the recomputation adds 4*d more).
+ */
+int attn_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int H_q, int H_kv,
+                  int N_q, int N_kv, int d, int causal, float scale, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_string(int status);
 

@@ -156,3 +156,20 @@ def test_fp8_decode_argument_errors():
     assert f8(Hq=12, Hkv=8) == 3
     assert f8(B=0) == 0
     assert f8() == 7 and f8(Nq=5) == 7
+
+
+def bw(dtype=E.ATTN_BF16, ws=P(0x7000000000), wsb=1 << 20, causal=0, **kw):
+    a = dict(B=1, Hq=2, Hkv=1, Nq=8, Nkv=8, d=64)
+    a.update(kw)
+    return L.attn_backward(FAKE[0], FAKE[1], FAKE[2], P(0x3000000), P(0x3100000), P(0x3200000),
+                           P(0x5000000), P(0x5100000), P(0x5200000), a["B"], a["Hq"], a["Hkv"],
+                           a["Nq"], a["Nkv"], a["d"], causal, 0.125, dtype, ws, wsb, None)
+
+
+def test_backward_argument_errors():
+    assert L.attn_backward_workspace_size(2, 8, 2, 100, 50, 128, E.ATTN_BF16) == 2 * 2 * 8 * 100 * 4
+    assert bw(dtype=E.ATTN_F32) == 4 and bw(d=96) == 4
+    assert bw(Hq=3, Hkv=2) == 3 and bw(causal=3) == 9
+    assert bw(ws=None) == 5 and bw(wsb=4) == 5
+    assert bw(B=0) == 0
+    assert bw() == 7 and bw(Nkv=0) == 7
