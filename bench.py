@@ -14,6 +14,8 @@ Default run (one JSON line on stdout):
   * "decode_paged" times the same caches cut into 16-position blocks scattered
     over a pool and read through a block table;
   * "decode_fp8" times the same caches stored as FP8 E4M3 codes (half the bytes);
+  * "backward" times the gradient of the prefill workload (dQ, dK, dV) in
+    TFLOP/s of 10*d FLOP per visible pair per head;
   * "cpu_baseline" times the float64 oracle on a bounded sample of the prefill
     workload on this host's cores.
 `--all` also times the other three workloads (fp32 single head, the 23,400-step
@@ -223,6 +225,32 @@ def bench_decode_fp8(cfg, steps, warmup, torch, E, cache, k_scale=2.0 ** -6, v_s
             "peak_gb_per_s": PEAK_HBM, "wall_s": wall}
 
 
+def bench_backward(cfg, steps, warmup, torch, E):
+    """Time one backward pass (Delta prep, dK/dV, dQ) of a prefill workload, given
+    the forward's O and LSE; TFLOP/s of 10*d FLOP per visible pair per head (the
+    five products of the gradient; the recomputation adds 4*d more)."""
+    q = make_device_tensor(cfg, "q", torch)
+    k = make_device_tensor(cfg, "k", torch)
+    v = make_device_tensor(cfg, "v", torch)
+    o, lse = E.attn_prefill_fwd(q, k, v, causal=cfg.causal, scale=cfg.scale, return_lse=True)
+    do = torch.randn_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(E.attn_backward_workspace_size(cfg.B, cfg.H_q, cfg.H_kv, cfg.N_q, cfg.N_kv, cfg.d,
+                                                    q.dtype), dtype=torch.uint8, device="cuda")
+
+    def call():
+        E.attn_backward(q, k, v, o, do, lse, dq, dk, dv, causal=cfg.causal, scale=cfg.scale,
+                        workspace=ws)
+
+    ms, wall = time_launches(call, steps, warmup, torch)
+    flops = prefill_flops(cfg) * 10 // 4
+    tflops = flops / (ms * 1e-3) / 1e12
+    del q, k, v, o, do, dq, dk, dv, ws
+    return {"config": f"{cfg.cid}-bwd", "name": cfg.name + ", backward", "ms": ms, "flops": flops,
+            "tflops": tflops, "frac_of_peak": tflops / PEAK_MFMA_16BIT, "peak_tflops": PEAK_MFMA_16BIT,
+            "wall_s": wall}
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=3):
     """A plain device-to-device copy of known size (torch's copy kernel): the
     HBM counters read for it calibrate the FETCH_SIZE / WRITE_SIZE scale."""
@@ -295,7 +323,7 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="also time configs 1, 3, 4 and ragged decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["prefill", "decode", "decode_ragged", "decode_multi",
-                                       "decode_paged", "decode_fp8"], default=None)
+                                       "decode_paged", "decode_fp8", "backward"], default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for HBM counter calibration)")
@@ -322,6 +350,10 @@ def main(argv=None):
         res["prefill"] = bench_prefill(A.CONFIGS[2], args.steps, args.warmup, torch, E)
         print(f"# prefill c2: {res['prefill']['ms']:.3f} ms  {res['prefill']['tflops']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
+    if args.only in (None, "backward"):
+        r = bench_backward(A.CONFIGS[2], args.steps, args.warmup, torch, E)
+        print(f"# backward c2: {r['ms']:.3f} ms  {r['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        res["backward"] = r
     cache = None
     if args.only in (None, "decode"):
         res["decode"], cache = bench_decode(A.CONFIGS[5], args.steps, args.warmup, torch, E)
@@ -374,6 +406,8 @@ def main(argv=None):
 
     p = res.get("prefill")
     d = res.get("decode")
+    if p is None and d is None:   # --only backward: its own line
+        p = dict(res["backward"], first_call_ms=0.0)
     main_r = p if p is not None else d
     line = {
         "metric": "prefill attention TFLOP/s and decode KV GB/s, as % of MI355X MFMA/HBM peak",
@@ -429,6 +463,14 @@ def main(argv=None):
             "ms_per_step": round(df8["ms"], 5), "value": round(df8["gb_per_s"], 2), "unit": "GB/s",
             "frac_of_hbm_peak": round(df8["frac_of_peak"], 4),
             "kernel": "decode_split_kernel<fp8> + decode_merge_kernel (one step)"}
+    bw = res.get("backward")
+    if bw:
+        line["backward"] = {
+            "workload": "backward of causal MHA prefill, bf16, B=4, H_q=H_kv=32, N=4096, d=128 "
+                        "(given the forward's O and LSE)",
+            "ms_per_step": round(bw["ms"], 5), "value": round(bw["tflops"], 2), "unit": "TFLOP/s",
+            "frac_of_mfma_peak": round(bw["frac_of_peak"], 4), "work_per_launch": bw["flops"],
+            "kernel": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel (one step)"}
     if p:
         line["prefill_first_call_ms"] = round(p["first_call_ms"], 3)
     if cpu:
