@@ -110,7 +110,9 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
     return ATTN_ERR_ALIAS;
   st = check_device();
   if (st != ATTN_OK) return st;
-  attn::PrefillArgs a{q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale, dtype};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  attn::PrefillArgs a{q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale, dtype, g_dev_cus[dev]};
   return attn::launch_prefill(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -21,6 +21,7 @@ struct PrefillArgs {
   int causal;
   float scale;
   int dtype;
+  int num_cus;  // compute units of the device (sizes persistent grids)
 };
 
 struct DecodeArgs {

@@ -87,7 +87,7 @@ template <int QB, int D> struct Occ {
   static constexpr int kWaves = (QB == 2 && D == 128) ? 1 : 2;  // wavefronts per SIMD
 };
 
-template <class TT, int D, bool CAUSAL, int QB, int NW = 4>
+template <class TT, int D, bool CAUSAL, int QB, int NW = 4, bool PERSIST = false>
 __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void prefill16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
@@ -110,9 +110,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  // causal: longest query blocks first
-  const WorkItem wi = map_work(nqb, H_q, nbatch, CAUSAL);
-  if (!wi.valid) return;
+  // one work item: query block qblk of head h of batch b
+  auto run = [&](const WorkItem wi) {
   const int qblk = wi.qblk, h = wi.h, b = wi.b;
   const int hk = h / (H_q / H_kv);
 
@@ -245,15 +244,17 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
       // ---- mask (tail and causal diagonal tiles only), branch-free per element
       const bool need_mask = (kv0 + kBN > N_kv) || (CAUSAL && kv0 + kBN - 1 > q0 + off);
       if (need_mask) {
-        const int kvb = kv0 + 4 * lh;
 #pragma unroll
-        for (int j = 0; j < QB; ++j)
+        for (int j = 0; j < QB; ++j) {
+          // key kv0 + 4*lh + c (c a per-register constant) is visible iff c < rel
+          const int rel = lim[j] - (kv0 + 4 * lh);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int kv = kvb + 8 * (r >> 2) + (r & 3);
-            s[j][0][r] = (kv < lim[j]) ? s[j][0][r] : kNegInf;
-            s[j][1][r] = (kv + 32 < lim[j]) ? s[j][1][r] : kNegInf;
+            const int c = 8 * (r >> 2) + (r & 3);
+            s[j][0][r] = (c < rel) ? s[j][0][r] : kNegInf;
+            s[j][1][r] = (c + 32 < rel) ? s[j][1][r] : kNegInf;
           }
+        }
       }
       uint32_t pk[QB][16];
 #pragma unroll
@@ -328,6 +329,38 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
     }
     if (LSE != nullptr && lh == 0 && qrow[j] < N_q) {
       LSE[((int64_t)b * H_q + h) * N_q + qrow[j]] = (lt > 0.f) ? (m[j] + log2f(lt)) * kLn2 : kNegInf;
+    }
+  }
+  };
+  if constexpr (!PERSIST) {
+    // one item per workgroup; causal: longest query blocks first
+    const WorkItem wi = map_work(nqb, H_q, nbatch, CAUSAL);
+    if (!wi.valid) return;
+    run(wi);
+  } else {
+    // Persistent: the grid holds as many workgroups as can be resident, and
+    // each walks items of its XCD's contiguous range (the same ranges as
+    // map_work). Slot s of an XCD takes items s, then 2*nslots - 1 - s, then
+    // 2*nslots + s, ...: a zig-zag, so that with causal masking (items of a
+    // head ordered longest first) every slot gets a mix of long and short
+    // query blocks. Workgroups no longer wait to be dispatched between items.
+    const int total = nqb * H_q * nbatch;
+    const int per_xcd = (total + 7) >> 3;
+    const int x = blockIdx.x & 7, nslots = (int)gridDim.x >> 3, slot = (int)blockIdx.x >> 3;
+    for (int r = 0;; ++r) {
+      const int it = r * nslots + ((r & 1) ? (nslots - 1 - slot) : slot);
+      if (it >= per_xcd) break;
+      const int item = x * per_xcd + it;
+      if (item >= total) break;
+      WorkItem w;
+      w.valid = true;
+      const int unit = item / nqb;
+      const int qi = item - unit * nqb;
+      w.qblk = CAUSAL ? (nqb - 1 - qi) : qi;
+      w.b = unit / H_q;
+      w.h = unit - w.b * H_q;
+      run(w);
+      __syncthreads();  // LDS tiles of this item are no longer read
     }
   }
 }
@@ -1340,6 +1373,49 @@ __global__ __launch_bounds__(kThreads, 2) void prefill32_kernel(
 // 1-D grid covering `items` work items, rounded up to a multiple of the 8 XCDs.
 inline int xcd_grid(int64_t items) { return (int)(((items + 7) / 8) * 8); }
 
+// Persistent launch of the default kernel: one workgroup per resident slot
+// (occupancy from the runtime, times the compute units), at most one per item.
+// With fewer than four items per slot the static zig-zag cannot balance
+// causal items of very different lengths, and the hardware's dynamic dispatch
+// of one item per workgroup does better; the persistent grid is used above that.
+template <class TT, int D, int NW, bool CAUSAL>
+hipError_t launch16pers_t(const PrefillArgs& a, hipStream_t st, int nqb) {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill16_kernel<TT, D, CAUSAL, 1, NW, true>,
+                                                     64 * NW, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  const int64_t items = (int64_t)nqb * a.H_q * a.B;
+  int64_t slots = (int64_t)per_cu * (a.num_cus > 0 ? a.num_cus : 256);
+  // tuning and testing: ATTN_PREFILL_SLOTS = n forces the persistent grid with n slots
+  const char* env = getenv("ATTN_PREFILL_SLOTS");
+  const int64_t forced = env ? atol(env) : 0;
+  if (forced > 0) slots = forced < slots ? forced : slots;
+  const float sl2 = a.scale * kLog2e;
+  if (forced <= 0 && items < 4 * slots) {
+    hipLaunchKernelGGL((prefill16_kernel<TT, D, CAUSAL, 1, NW, false>), dim3(xcd_grid(items)),
+                       dim3(64 * NW), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2,
+                       nqb, a.B);
+  } else {
+    hipLaunchKernelGGL((prefill16_kernel<TT, D, CAUSAL, 1, NW, true>), dim3(xcd_grid(slots)),
+                       dim3(64 * NW), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2,
+                       nqb, a.B);
+  }
+  return hipGetLastError();
+}
+
+template <class TT, int D, int NW>
+hipError_t launch16pers(const PrefillArgs& a, hipStream_t st) {
+  const int nqb = (a.N_q + NW * 32 - 1) / (NW * 32);
+  return a.causal ? launch16pers_t<TT, D, NW, true>(a, st, nqb)
+                  : launch16pers_t<TT, D, NW, false>(a, st, nqb);
+}
+
 template <class TT, int D, int QB, int NW = 4>
 hipError_t launch16q(const PrefillArgs& a, hipStream_t st) {
   constexpr int BM = NW * 32 * QB;
@@ -1437,13 +1513,12 @@ hipError_t launch16w2(const PrefillArgs& a, hipStream_t st) {
 // SIMD instead. ATTN_PREFILL_VARIANT selects alternative forms (tuning only):
 // 1 = 4 wavefronts, 2 = two query blocks per wavefront, 3 = software-pipelined
 // scores, 4 = two ping-ponging wavefront groups, 5 = direct-load 3-stage ring,
-// 6 = two query blocks with a direct-load ring, 7 = 8 wavefronts.
+// 6 = two query blocks with a direct-load ring, 7 = 8 wavefronts, 8 = the
+// default kernel with one work item per workgroup instead of a persistent grid.
 template <class TT, int D>
 hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
-  static const int variant = [] {
-    const char* e = getenv("ATTN_PREFILL_VARIANT");
-    return e ? atoi(e) : 0;
-  }();
+  const char* env = getenv("ATTN_PREFILL_VARIANT");
+  const int variant = env ? atoi(env) : 0;
   if (variant == 2) return launch16q<TT, D, 2>(a, st);
   if (variant == 3) return launch16p<TT, D>(a, st);
   if (variant == 4) return launch16pp<TT, D>(a, st);
@@ -1451,7 +1526,8 @@ hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
   if (variant == 1) return launch16q<TT, D, 1, 4>(a, st);
   if (variant == 6) return launch16w2<TT, D>(a, st);
   if (variant == 7) return launch16q<TT, D, 1, 8>(a, st);
-  return launch16q<TT, D, 1, (D == 128 ? 8 : 4)>(a, st);
+  if (variant == 8) return launch16q<TT, D, 1, (D == 128 ? 8 : 4)>(a, st);
+  return launch16pers<TT, D, (D == 128 ? 8 : 4)>(a, st);
 }
 
 template <int D>

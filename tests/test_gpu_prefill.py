@@ -155,3 +155,30 @@ def test_prefill_full_size_sampled(cid):
         check_lse(lse[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64), lref,
                   TOL_LSE[cfg.dtype])
     print(f"config {cid}: worst sampled max|err| = {worst:.3e}", flush=True)
+
+
+# more work items than workgroups: a persistent grid walks several items per
+# workgroup (d = 128: one workgroup per compute unit; d = 64: three)
+MANY_ITEMS = [(2, 64, 64, 700, 700, 128), (4, 64, 16, 500, 500, 64), (1, 48, 8, 1100, 2000, 128)]
+
+
+@pytest.mark.parametrize("slots", [None, "16", "8"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", MANY_ITEMS, ids=lambda s: "x".join(map(str, s)))
+def test_prefill_persistent_grid_many_items(shape, causal, slots, monkeypatch):
+    """Several items per workgroup: a persistent grid of 8 or 16 workgroups (or
+    the automatic choice) walks every query block exactly once."""
+    if slots is not None:
+        monkeypatch.setenv("ATTN_PREFILL_SLOTS", slots)
+    _run_small(*shape, "bf16", causal, seed=zlib.crc32(repr((shape, causal)).encode()) % 10000)
+
+
+@pytest.mark.parametrize("variant", ["1", "2", "3", "4", "5", "6", "7", "8"])
+def test_prefill_variants_match_oracle(variant, monkeypatch):
+    """Every alternative kernel behind ATTN_PREFILL_VARIANT (tuning only) meets
+    the same bar as the default."""
+    monkeypatch.setenv("ATTN_PREFILL_VARIANT", variant)
+    for i, (shape, causal, dtype) in enumerate([
+            ((1, 4, 2, 300, 300, 128), True, "bf16"), ((2, 2, 2, 129, 257, 64), True, "f16"),
+            ((1, 8, 8, 200, 200, 128), False, "f16"), ((1, 2, 1, 70, 30, 64), True, "bf16")]):
+        _run_small(*shape, dtype, causal, seed=100 + 10 * int(variant) + i)
