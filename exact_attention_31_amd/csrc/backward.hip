@@ -305,7 +305,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ. Workgroup: 32*NW query rows of head h of batch b; lane: query row
+// dQ. Two resident workgroups per compute unit (registers capped so that two
+// wavefronts share each SIMD). Workgroup: 32*NW query rows of head h of batch b; lane: query row
 // q0 + lane % 32 as the B operand column of S^T = K Q^T and dP^T = V dO^T.
 // Key tiles of 64 rows stream through LDS (double-buffered, register-staged).
 // Per 32-key half:
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 //   P^T, dS^T per element (one lse2 and Delta per lane)
 //   dQ^T += K^T dS^T                     (A: K^T by transposing LDS reads; B: dS^T)
 template <class TT, int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
     uint16_t* __restrict__ dQ, int H_q, int H_kv, int N_q, int N_kv, float scale_log2, float scale,
