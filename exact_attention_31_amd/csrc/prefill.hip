@@ -110,41 +110,79 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  // one work item: query block qblk of head h of batch b
-  auto run = [&](const WorkItem wi) {
-  const int qblk = wi.qblk, h = wi.h, b = wi.b;
-  const int hk = h / (H_q / H_kv);
-
+  const int off = N_kv - N_q;  // bottom-right causal alignment
   const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
   const uint32_t head_kv_bytes = (uint32_t)N_kv * D * 2;
-  const auto rQ = buffer_rsrc(Q + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
-  const auto rK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-  const auto rV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
 
-  const int q0 = qblk * BM + wave * 32 * QB;  // first row of this wavefront
-  const int off = N_kv - N_q;                 // bottom-right causal alignment
-  int qrow[QB], lim[QB];
+  // ---- work items. One per workgroup (map_work), or, persistent: the grid
+  // holds as many workgroups as can be resident, and each walks items of its
+  // XCD's contiguous range (the same ranges as map_work). Slot s of an XCD
+  // takes items s, then 2*nslots - 1 - s, then 2*nslots + s, ...: a zig-zag, so
+  // that with causal masking (items of a head ordered longest first) every
+  // slot gets a mix of long and short query blocks.
+  int round = 0;
+  auto next_item = [&](WorkItem& w) -> bool {
+    if constexpr (!PERSIST) {
+      if (round++ > 0) return false;
+      w = map_work(nqb, H_q, nbatch, CAUSAL);
+      return w.valid;
+    } else {
+      const int total = nqb * H_q * nbatch;
+      const int per_xcd = (total + 7) >> 3;
+      const int nslots = (int)gridDim.x >> 3, slot = (int)blockIdx.x >> 3;
+      const int r = round++;
+      const int it = r * nslots + ((r & 1) ? (nslots - 1 - slot) : slot);
+      const int item = (int)(blockIdx.x & 7) * per_xcd + it;
+      if (it >= per_xcd || item >= total) return false;
+      const int unit = item / nqb;
+      const int qi = item - unit * nqb;
+      w.valid = true;
+      w.qblk = CAUSAL ? (nqb - 1 - qi) : qi;
+      w.b = unit / H_q;
+      w.h = unit - w.b * H_q;
+      return true;
+    }
+  };
+  // per-item addressing and bounds
+  struct Ctx {
+    __amdgpu_buffer_rsrc_t rQ, rK, rV;
+    int b, h, qblk, q0, ntiles;
+    int qrow[QB], lim[QB];
+  };
+  auto ctx_of = [&](const WorkItem& wi) {
+    Ctx c;
+    c.b = wi.b;
+    c.h = wi.h;
+    c.qblk = wi.qblk;
+    const int hk = wi.h / (H_q / H_kv);
+    c.rQ = buffer_rsrc(Q + ((int64_t)wi.b * H_q + wi.h) * (int64_t)N_q * D, head_q_bytes);
+    c.rK = buffer_rsrc(K + ((int64_t)wi.b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
+    c.rV = buffer_rsrc(V + ((int64_t)wi.b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
+    c.q0 = wi.qblk * BM + wave * 32 * QB;  // first row of this wavefront
 #pragma unroll
-  for (int j = 0; j < QB; ++j) {
-    qrow[j] = q0 + 32 * j + lr;  // this lane's row in query block j
-    // keys below lim[j] are visible to that row
-    lim[j] = CAUSAL ? min(N_kv, max(qrow[j] + off + 1, 0)) : N_kv;
-  }
+    for (int j = 0; j < QB; ++j) {
+      c.qrow[j] = c.q0 + 32 * j + lr;  // this lane's row in query block j
+      // keys below lim[j] are visible to that row
+      c.lim[j] = CAUSAL ? min(N_kv, max(c.qrow[j] + off + 1, 0)) : N_kv;
+    }
+    int kv_end = N_kv;
+    if (CAUSAL) {
+      const int qlast = min(wi.qblk * BM + BM - 1, N_q - 1);
+      kv_end = min(N_kv, qlast + off + 1);
+    }
+    c.ntiles = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
+    return c;
+  };
 
   // Q^T operand: lane holds row qrow[j], d = 16*s + 8*lh + 0..7 (rows past N_q read as 0)
   u32x4_t qreg[QB][KS];
+  auto load_q = [&](const Ctx& c) {
 #pragma unroll
-  for (int j = 0; j < QB; ++j)
+    for (int j = 0; j < QB; ++j)
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qreg[j][s] = buffer_load16(rQ, (uint32_t)(qrow[j] * D + 16 * s + 8 * lh) * 2);
-
-  int kv_end = N_kv;
-  if (CAUSAL) {
-    const int qlast = min(qblk * BM + BM - 1, N_q - 1);
-    kv_end = min(N_kv, qlast + off + 1);
-  }
-  const int ntiles = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
+      for (int s = 0; s < KS; ++s)
+        qreg[j][s] = buffer_load16(c.rQ, (uint32_t)(c.qrow[j] * D + 16 * s + 8 * lh) * 2);
+  };
 
   // this thread's share of each tile: chunk c = tid + NT*i -> row c / CPR, column c % CPR
   uint32_t ld_off[LPT];
@@ -165,12 +203,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
   const int v_lane = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * VST + 16 * ((lane >> 4) & 1) +
                      4 * (lane & 3);
   u32x4_t kbuf[LPT], vbuf[LPT];
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](const Ctx& c, int t) {
     const uint32_t base = (uint32_t)(t * kBN) * D * 2;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      kbuf[i] = buffer_load16(rK, base + ld_off[i]);
-      vbuf[i] = buffer_load16(rV, base + ld_off[i]);
+      kbuf[i] = buffer_load16(c.rK, base + ld_off[i]);
+      vbuf[i] = buffer_load16(c.rV, base + ld_off[i]);
     }
   };
   auto store_tile = [&](int buf) {
@@ -181,187 +219,183 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
     }
   };
 
-  f32x16_t oacc[QB][DB];
-  float m[QB], l[QB];
-#pragma unroll
-  for (int j = 0; j < QB; ++j) {
-#pragma unroll
-    for (int i = 0; i < DB; ++i) oacc[j][i] = f32x16_t{0};
-    m[j] = kNegInf;  // reference maximum, in units of log2 (scores * scale * log2 e)
-    l[j] = 0.f;      // this half-wave's part of the denominator
-  }
-
+  WorkItem first;
+  if (!next_item(first)) return;
+  Ctx c = ctx_of(first);
   // Tile 0 is staged unconditionally (loads past the end read zeros): with no
   // branch here every load issued so far has completed when the loop starts,
   // so the loop only ever waits for its own prefetch, at the LDS store.
-  load_tile(0);
+  load_q(c);
+  load_tile(c, 0);
   store_tile(0);
   vmem_wait_all();
   __syncthreads();
+  int par = 0;  // LDS buffer holding the current item's tile 0
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);  // in flight during this tile's math
-    const int kv0 = t * kBN;
-    // wavefront-uniform: does this tile hold any key visible to this wavefront?
-    const bool live = !CAUSAL || kv0 <= q0 + 32 * QB - 1 + off;
-    if (live) {
-      const uint16_t* tK = &sK[0][0] + buf * (kBN * KST) + k_lane;
-      const uint16_t* tV = &sV[0][0] + buf * (kBN * VST) + v_lane;
-      // ---- S^T = K Q^T: two 32-key blocks x QB query blocks; each K read feeds QB MFMAs
-      f32x16_t s[QB][2];
+  for (;;) {
+    // The next item's tile 0 is loaded during this item's last tile, and its
+    // Q rows at the end of that tile, so that the next item starts with its
+    // operands in place.
+    WorkItem nwi;
+    const bool has_next = next_item(nwi);
+    const Ctx cn = has_next ? ctx_of(nwi) : c;
+
+    f32x16_t oacc[QB][DB];
+    float m[QB], l[QB];
 #pragma unroll
-      for (int j = 0; j < QB; ++j) s[j][0] = s[j][1] = f32x16_t{0};
+    for (int j = 0; j < QB; ++j) {
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const u32x4_t a0 = *(const u32x4_t*)(tK + 16 * st);
-        const u32x4_t a1 = *(const u32x4_t*)(tK + 32 * KST + 16 * st);
+      for (int i = 0; i < DB; ++i) oacc[j][i] = f32x16_t{0};
+      m[j] = kNegInf;  // reference maximum, in units of log2 (scores * scale * log2 e)
+      l[j] = 0.f;      // this half-wave's part of the denominator
+    }
+    const int ntiles = c.ntiles, q0 = c.q0;
+
+    for (int t = 0; t < ntiles; ++t) {
+      const int buf = (t + par) & 1;
+      const bool last = t + 1 == ntiles;
+      if (!last) load_tile(c, t + 1);  // in flight during this tile's math
+      else if (has_next) load_tile(cn, 0);
+      const int kv0 = t * kBN;
+      // wavefront-uniform: does this tile hold any key visible to this wavefront?
+      const bool live = !CAUSAL || kv0 <= q0 + 32 * QB - 1 + off;
+      if (live) {
+        const uint16_t* tK = &sK[0][0] + buf * (kBN * KST) + k_lane;
+        const uint16_t* tV = &sV[0][0] + buf * (kBN * VST) + v_lane;
+        // ---- S^T = K Q^T: two 32-key blocks x QB query blocks; each K read feeds QB MFMAs
+        f32x16_t s[QB][2];
 #pragma unroll
-        for (int j = 0; j < QB; ++j) {
-          s[j][0] = TT::mfma32(a0, qreg[j][st], s[j][0]);
-          s[j][1] = TT::mfma32(a1, qreg[j][st], s[j][1]);
-        }
-      }
-      // keep the K operand reads two k-steps ahead of the MFMAs that use them
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        for (int j = 0; j < QB; ++j) s[j][0] = s[j][1] = f32x16_t{0};
 #pragma unroll
-      for (int st = 0; st < KS - 2; ++st) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * QB, 0);
-      // V^T operands of this tile, requested now so that the score MFMAs, the
-      // row max and the exponentials cover their LDS latency
-      u32x4_t vop[4][DB];
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2_t lo = lds_read_tr16(tV + 16 * t4 * VST + db * 32);
-          const u32x2_t hi = lds_read_tr16(tV + (16 * t4 + 8) * VST + db * 32);
-          vop[t4][db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-        }
-      // ---- mask (tail and causal diagonal tiles only), branch-free per element
-      const bool need_mask = (kv0 + kBN > N_kv) || (CAUSAL && kv0 + kBN - 1 > q0 + off);
-      if (need_mask) {
-#pragma unroll
-        for (int j = 0; j < QB; ++j) {
-          // key kv0 + 4*lh + c (c a per-register constant) is visible iff c < rel
-          const int rel = lim[j] - (kv0 + 4 * lh);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int c = 8 * (r >> 2) + (r & 3);
-            s[j][0][r] = (c < rel) ? s[j][0][r] : kNegInf;
-            s[j][1][r] = (c + 32 < rel) ? s[j][1][r] : kNegInf;
-          }
-        }
-      }
-      uint32_t pk[QB][16];
-#pragma unroll
-      for (int j = 0; j < QB; ++j) {
-        // ---- row max of the raw scores (scale > 0 commutes with max)
-        float mx = max3(s[j][0][0], s[j][0][1], s[j][1][0]);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = max3(mx, s[j][0][r], s[j][1][r]);
-        mx = fmaxf(mx, s[j][1][0]);
-        const float mxs = half_max(mx) * scale_log2;
-        // The branch is wavefront-uniform, but each lane moves only its own
-        // reference (alpha = 1 is an exact multiply), so a row's arithmetic never
-        // depends on the other rows of the wavefront.
-        const bool need = mxs > m[j] + kLazyRescale;
-        if (wave_any(need)) {
-          const float alpha = need ? ((m[j] == kNegInf) ? 0.f : fast_exp2(m[j] - mxs)) : 1.f;
-          m[j] = need ? mxs : m[j];
-          l[j] *= alpha;
-#pragma unroll
-          for (int i = 0; i < DB; ++i) oacc[j][i] *= alpha;
-        }
-        const float nm = (m[j] == kNegInf) ? 0.f : -m[j];
-        // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[j][0][r], scale_log2, nm));
-          const float p1 = fast_exp2(__builtin_fmaf(s[j][0][r + 1], scale_log2, nm));
-          const float p2 = fast_exp2(__builtin_fmaf(s[j][1][r], scale_log2, nm));
-          const float p3 = fast_exp2(__builtin_fmaf(s[j][1][r + 1], scale_log2, nm));
-          l[j] += (p0 + p1) + (p2 + p3);
-          pk[j][r >> 1] = TT::pack2(p0, p1);
-          pk[j][8 + (r >> 1)] = TT::pack2(p2, p3);
-        }
-      }
-      // ---- O^T += V^T P^T, four 16-key steps; V^T through the transposing LDS read,
-      // each V operand feeding QB MFMAs
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          // key rows 16*t4 + 4*lh + {0..3} (then + 8), columns db*32 + this lane's 16-group
-          const u32x4_t aop = vop[t4][db];
+        for (int st = 0; st < KS; ++st) {
+          const u32x4_t a0 = *(const u32x4_t*)(tK + 16 * st);
+          const u32x4_t a1 = *(const u32x4_t*)(tK + 32 * KST + 16 * st);
 #pragma unroll
           for (int j = 0; j < QB; ++j) {
-            const u32x4_t bop = {pk[j][4 * t4 + 0], pk[j][4 * t4 + 1], pk[j][4 * t4 + 2],
-                                 pk[j][4 * t4 + 3]};
-            oacc[j][db] = TT::mfma32(aop, bop, oacc[j][db]);
+            s[j][0] = TT::mfma32(a0, qreg[j][st], s[j][0]);
+            s[j][1] = TT::mfma32(a1, qreg[j][st], s[j][1]);
+          }
+        }
+        // keep the K operand reads two k-steps ahead of the MFMAs that use them
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int st = 0; st < KS - 2; ++st) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * QB, 0);
+        // V^T operands of this tile, requested now so that the score MFMAs, the
+        // row max and the exponentials cover their LDS latency
+        u32x4_t vop[4][DB];
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const u32x2_t lo = lds_read_tr16(tV + 16 * t4 * VST + db * 32);
+            const u32x2_t hi = lds_read_tr16(tV + (16 * t4 + 8) * VST + db * 32);
+            vop[t4][db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          }
+        // ---- mask (tail and causal diagonal tiles only), branch-free per element
+        const bool need_mask = (kv0 + kBN > N_kv) || (CAUSAL && kv0 + kBN - 1 > q0 + off);
+        if (need_mask) {
+#pragma unroll
+          for (int j = 0; j < QB; ++j) {
+            // key kv0 + 4*lh + e (e a per-register constant) is visible iff e < rel
+            const int rel = c.lim[j] - (kv0 + 4 * lh);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int e = 8 * (r >> 2) + (r & 3);
+              s[j][0][r] = (e < rel) ? s[j][0][r] : kNegInf;
+              s[j][1][r] = (e + 32 < rel) ? s[j][1][r] : kNegInf;
+            }
+          }
+        }
+        uint32_t pk[QB][16];
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+          // ---- row max of the raw scores (scale > 0 commutes with max)
+          float mx = max3(s[j][0][0], s[j][0][1], s[j][1][0]);
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = max3(mx, s[j][0][r], s[j][1][r]);
+          mx = fmaxf(mx, s[j][1][0]);
+          const float mxs = half_max(mx) * scale_log2;
+          // The branch is wavefront-uniform, but each lane moves only its own
+          // reference (alpha = 1 is an exact multiply), so a row's arithmetic never
+          // depends on the other rows of the wavefront.
+          const bool need = mxs > m[j] + kLazyRescale;
+          if (wave_any(need)) {
+            const float alpha = need ? ((m[j] == kNegInf) ? 0.f : fast_exp2(m[j] - mxs)) : 1.f;
+            m[j] = need ? mxs : m[j];
+            l[j] *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i) oacc[j][i] *= alpha;
+          }
+          const float nm = (m[j] == kNegInf) ? 0.f : -m[j];
+          // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(__builtin_fmaf(s[j][0][r], scale_log2, nm));
+            const float p1 = fast_exp2(__builtin_fmaf(s[j][0][r + 1], scale_log2, nm));
+            const float p2 = fast_exp2(__builtin_fmaf(s[j][1][r], scale_log2, nm));
+            const float p3 = fast_exp2(__builtin_fmaf(s[j][1][r + 1], scale_log2, nm));
+            l[j] += (p0 + p1) + (p2 + p3);
+            pk[j][r >> 1] = TT::pack2(p0, p1);
+            pk[j][8 + (r >> 1)] = TT::pack2(p2, p3);
+          }
+        }
+        // ---- O^T += V^T P^T, four 16-key steps; V^T through the transposing LDS read,
+        // each V operand feeding QB MFMAs
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            // key rows 16*t4 + 4*lh + {0..3} (then + 8), columns db*32 + this lane's 16-group
+            const u32x4_t aop = vop[t4][db];
+#pragma unroll
+            for (int j = 0; j < QB; ++j) {
+              const u32x4_t bop = {pk[j][4 * t4 + 0], pk[j][4 * t4 + 1], pk[j][4 * t4 + 2],
+                                   pk[j][4 * t4 + 3]};
+              oacc[j][db] = TT::mfma32(aop, bop, oacc[j][db]);
+            }
           }
         }
       }
-
+      if (!last || has_next) store_tile(buf ^ 1);
+      if (last && has_next) load_q(cn);  // this item's Q is no longer read
+      __syncthreads();
     }
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
-  }
+    if (ntiles == 0 && has_next) {  // no keys: stage the next item here
+      load_q(cn);
+      load_tile(cn, 0);
+      store_tile(par ^ 1);
+    }
 
-  // ---- epilogue: combine half-wave denominators, normalise, store (rows past N_q dropped)
-  const auto rO = buffer_rsrc(O + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
+    // ---- epilogue: combine half-wave denominators, normalise, store (rows past N_q dropped)
+    const auto rO = buffer_rsrc(O + ((int64_t)c.b * H_q + c.h) * (int64_t)N_q * D, head_q_bytes);
 #pragma unroll
-  for (int j = 0; j < QB; ++j) {
-    const float lt = half_sum(l[j]);
-    const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+    for (int j = 0; j < QB; ++j) {
+      const float lt = half_sum(l[j]);
+      const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+      for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d = db * 32 + 8 * rg + 4 * lh;
-        const u32x2_t w = {TT::pack2(oacc[j][db][4 * rg + 0] * inv, oacc[j][db][4 * rg + 1] * inv),
-                           TT::pack2(oacc[j][db][4 * rg + 2] * inv, oacc[j][db][4 * rg + 3] * inv)};
-        buffer_store8(rO, (uint32_t)(qrow[j] * D + d) * 2, w);
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d = db * 32 + 8 * rg + 4 * lh;
+          const u32x2_t w = {TT::pack2(oacc[j][db][4 * rg + 0] * inv, oacc[j][db][4 * rg + 1] * inv),
+                             TT::pack2(oacc[j][db][4 * rg + 2] * inv, oacc[j][db][4 * rg + 3] * inv)};
+          buffer_store8(rO, (uint32_t)(c.qrow[j] * D + d) * 2, w);
+        }
+      }
+      if (LSE != nullptr && lh == 0 && c.qrow[j] < N_q) {
+        LSE[((int64_t)c.b * H_q + c.h) * N_q + c.qrow[j]] =
+            (lt > 0.f) ? (m[j] + log2f(lt)) * kLn2 : kNegInf;
       }
     }
-    if (LSE != nullptr && lh == 0 && qrow[j] < N_q) {
-      LSE[((int64_t)b * H_q + h) * N_q + qrow[j]] = (lt > 0.f) ? (m[j] + log2f(lt)) * kLn2 : kNegInf;
-    }
-  }
-  };
-  if constexpr (!PERSIST) {
-    // one item per workgroup; causal: longest query blocks first
-    const WorkItem wi = map_work(nqb, H_q, nbatch, CAUSAL);
-    if (!wi.valid) return;
-    run(wi);
-  } else {
-    // Persistent: the grid holds as many workgroups as can be resident, and
-    // each walks items of its XCD's contiguous range (the same ranges as
-    // map_work). Slot s of an XCD takes items s, then 2*nslots - 1 - s, then
-    // 2*nslots + s, ...: a zig-zag, so that with causal masking (items of a
-    // head ordered longest first) every slot gets a mix of long and short
-    // query blocks. Workgroups no longer wait to be dispatched between items.
-    const int total = nqb * H_q * nbatch;
-    const int per_xcd = (total + 7) >> 3;
-    const int x = blockIdx.x & 7, nslots = (int)gridDim.x >> 3, slot = (int)blockIdx.x >> 3;
-    for (int r = 0;; ++r) {
-      const int it = r * nslots + ((r & 1) ? (nslots - 1 - slot) : slot);
-      if (it >= per_xcd) break;
-      const int item = x * per_xcd + it;
-      if (item >= total) break;
-      WorkItem w;
-      w.valid = true;
-      const int unit = item / nqb;
-      const int qi = item - unit * nqb;
-      w.qblk = CAUSAL ? (nqb - 1 - qi) : qi;
-      w.b = unit / H_q;
-      w.h = unit - w.b * H_q;
-      run(w);
-      __syncthreads();  // LDS tiles of this item are no longer read
-    }
+    if (!has_next) break;
+    vmem_wait_all();
+    __syncthreads();
+    par = (par + (ntiles > 0 ? ntiles : 1)) & 1;
+    c = cn;
   }
 }
 
