@@ -399,6 +399,225 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
   }
 }
 
+// Phase-skewed form: 8 wavefronts, two per SIMD (wavefronts w and w + 4 share
+// a SIMD). Group A (wavefronts 0-3) works tile t as S(t) -> softmax(t) ->
+// PV(t); group B (4-7) runs half a tile behind: softmax(t-1) -> PV(t-1) ->
+// S(t), carrying its scores across the barrier. So while one wavefront of a
+// SIMD turns scores into probabilities on the vector ALUs, the other keeps the
+// matrix cores busy, instead of both doing the same phase at once. V tiles are
+// read one iteration longer (by group B), so V has three LDS buffers and K two;
+// one extra iteration at the end lets group B finish the last tile.
+template <class TT, int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void prefill16_skew_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
+    float scale_log2, int nqb, int nbatch) {
+  constexpr int KST = Lds16<D>::kK;
+  constexpr int VST = Lds16<D>::kV;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int NT = 512;
+  constexpr int LPT = kBN * CPR / NT;
+  constexpr int BM = 256;
+  static_assert(LPT >= 1 && LPT * NT == kBN * CPR, "tile load must split evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * KST];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[3][kBN * VST];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool grpB = wave >= 4;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const WorkItem wi = map_work(nqb, H_q, nbatch, CAUSAL);
+  if (!wi.valid) return;
+  const int qblk = wi.qblk, h = wi.h, b = wi.b;
+  const int hk = h / (H_q / H_kv);
+  const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
+  const uint32_t head_kv_bytes = (uint32_t)N_kv * D * 2;
+  const auto rQ = buffer_rsrc(Q + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
+  const auto rK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
+  const auto rV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
+  const int q0 = qblk * BM + wave * 32;
+  const int off = N_kv - N_q;
+  const int qrow = q0 + lr;
+  const int lim = CAUSAL ? min(N_kv, max(qrow + off + 1, 0)) : N_kv;
+
+  u32x4_t qreg[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) qreg[st] = buffer_load16(rQ, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
+
+  int kv_end = N_kv;
+  if (CAUSAL) {
+    const int qlast = min(qblk * BM + BM - 1, N_q - 1);
+    kv_end = min(N_kv, qlast + off + 1);
+  }
+  const int ntiles = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
+
+  uint32_t ld_off[LPT];
+  int st_k[LPT], st_v[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int c = tid + NT * i;
+    const int r = c / CPR, cc = c % CPR;
+    ld_off[i] = (uint32_t)(r * D + cc * 8) * 2;
+    st_k[i] = r * KST + cc * 8;
+    st_v[i] = r * VST + cc * 8;
+  }
+  const int k_lane = lr * KST + 8 * lh;
+  const int v_lane = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * VST + 16 * ((lane >> 4) & 1) +
+                     4 * (lane & 3);
+  u32x4_t kbuf[LPT], vbuf[LPT];
+  auto load_tile = [&](int t) {
+    const uint32_t base = (uint32_t)(t * kBN) * D * 2;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      kbuf[i] = buffer_load16(rK, base + ld_off[i]);
+      vbuf[i] = buffer_load16(rV, base + ld_off[i]);
+    }
+  };
+  auto store_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      *(u32x4_t*)(&sK[t & 1][st_k[i]]) = kbuf[i];
+      *(u32x4_t*)(&sV[t % 3][st_v[i]]) = vbuf[i];
+    }
+  };
+
+  f32x16_t oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16_t{0};
+  float m = kNegInf, l = 0.f;
+
+  // does tile t hold any key visible to this wavefront?
+  auto live = [&](int t) { return !CAUSAL || t * kBN <= q0 + 31 + off; };
+  auto scores = [&](int t, f32x16_t& s0, f32x16_t& s1) {
+    const uint16_t* tK = &sK[t & 1][0] + k_lane;
+    s0 = f32x16_t{0};
+    s1 = f32x16_t{0};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const u32x4_t a0 = *(const u32x4_t*)(tK + 16 * st);
+      const u32x4_t a1 = *(const u32x4_t*)(tK + 32 * KST + 16 * st);
+      s0 = TT::mfma32(a0, qreg[st], s0);
+      s1 = TT::mfma32(a1, qreg[st], s1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int st = 0; st < KS - 2; ++st) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+  // softmax of the scores in s0/s1 (tile t) and O^T += V(t)^T P^T
+  auto softmax_pv = [&](int t, f32x16_t& s0, f32x16_t& s1) {
+    const uint16_t* tV = &sV[t % 3][0] + v_lane;
+    const int kv0 = t * kBN;
+    const bool need_mask = (kv0 + kBN > N_kv) || (CAUSAL && kv0 + kBN - 1 > q0 + off);
+    if (need_mask) {
+      const int rel = lim - (kv0 + 4 * lh);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = 8 * (r >> 2) + (r & 3);
+        s0[r] = (e < rel) ? s0[r] : kNegInf;
+        s1[r] = (e + 32 < rel) ? s1[r] : kNegInf;
+      }
+    }
+    float mx = max3(s0[0], s0[1], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = max3(mx, s0[r], s1[r]);
+    mx = fmaxf(mx, s1[0]);
+    const float mxs = half_max(mx) * scale_log2;
+    const bool need = mxs > m + kLazyRescale;
+    if (wave_any(need)) {
+      const float alpha = need ? ((m == kNegInf) ? 0.f : fast_exp2(m - mxs)) : 1.f;
+      m = need ? mxs : m;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+    }
+    const float nm = (m == kNegInf) ? 0.f : -m;
+    uint32_t pk[16];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = fast_exp2(__builtin_fmaf(s0[r], scale_log2, nm));
+      const float p1 = fast_exp2(__builtin_fmaf(s0[r + 1], scale_log2, nm));
+      const float p2 = fast_exp2(__builtin_fmaf(s1[r], scale_log2, nm));
+      const float p3 = fast_exp2(__builtin_fmaf(s1[r + 1], scale_log2, nm));
+      l += (p0 + p1) + (p2 + p3);
+      pk[r >> 1] = TT::pack2(p0, p1);
+      pk[8 + (r >> 1)] = TT::pack2(p2, p3);
+    }
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const u32x4_t bop = {pk[4 * t4 + 0], pk[4 * t4 + 1], pk[4 * t4 + 2], pk[4 * t4 + 3]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2_t lo = lds_read_tr16(tV + 16 * t4 * VST + db * 32);
+        const u32x2_t hi = lds_read_tr16(tV + (16 * t4 + 8) * VST + db * 32);
+        oacc[db] = TT::mfma32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, bop, oacc[db]);
+      }
+    }
+    // V operand reads two MFMAs ahead of their use
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * DB - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+
+  load_tile(0);
+  store_tile(0);
+  vmem_wait_all();
+  __syncthreads();
+
+  // The two groups run separate loops (so that group B's carried scores do not
+  // occupy registers in group A's code); both pass the same barriers.
+  const int niter = ntiles > 0 ? ntiles + 1 : 0;
+  if (grpB) {
+    f32x16_t c0 = f32x16_t{0}, c1 = f32x16_t{0};  // scores carried to the next iteration
+    for (int t = 0; t < niter; ++t) {
+      if (t + 1 < ntiles) load_tile(t + 1);
+      if (t >= 1 && live(t - 1)) softmax_pv(t - 1, c0, c1);
+      if (t < ntiles && live(t)) scores(t, c0, c1);
+      if (t + 1 < ntiles) store_tile(t + 1);
+      __syncthreads();
+    }
+  } else {
+    for (int t = 0; t < niter; ++t) {
+      if (t + 1 < ntiles) load_tile(t + 1);
+      if (t < ntiles && live(t)) {
+        f32x16_t a0, a1;
+        scores(t, a0, a1);
+        softmax_pv(t, a0, a1);
+      }
+      if (t + 1 < ntiles) store_tile(t + 1);
+      __syncthreads();
+    }
+  }
+
+  const auto rO = buffer_rsrc(O + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
+  const float lt = half_sum(l);
+  const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d = db * 32 + 8 * rg + 4 * lh;
+      const u32x2_t w = {TT::pack2(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv),
+                         TT::pack2(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv)};
+      buffer_store8(rO, (uint32_t)(qrow * D + d) * 2, w);
+    }
+  }
+  if (LSE != nullptr && lh == 0 && qrow < N_q) {
+    LSE[((int64_t)b * H_q + h) * N_q + qrow] = (lt > 0.f) ? (m + log2f(lt)) * kLn2 : kNegInf;
+  }
+}
+
 // Software-pipelined form (32 rows per wavefront). While the matrix cores
 // compute the scores of key tile t+1, the vector ALUs turn the scores of tile t
 // into probabilities; the products with V follow. K is staged in LDS one tile
@@ -1548,7 +1767,26 @@ hipError_t launch16w2(const PrefillArgs& a, hipStream_t st) {
 // 1 = 4 wavefronts, 2 = two query blocks per wavefront, 3 = software-pipelined
 // scores, 4 = two ping-ponging wavefront groups, 5 = direct-load 3-stage ring,
 // 6 = two query blocks with a direct-load ring, 7 = 8 wavefronts, 8 = the
-// default kernel with one work item per workgroup instead of a persistent grid.
+// default kernel with one work item per workgroup instead of a persistent grid,
+// 9 = two wavefront groups skewed by half a tile.
+template <class TT, int D>
+hipError_t launch16skew(const PrefillArgs& a, hipStream_t st) {
+  const int nqb = (a.N_q + 255) / 256;
+  dim3 grid(xcd_grid((int64_t)nqb * a.H_q * a.B));
+  const float sl2 = a.scale * kLog2e;
+  auto q = (const uint16_t*)a.q;
+  auto k = (const uint16_t*)a.k;
+  auto v = (const uint16_t*)a.v;
+  auto o = (uint16_t*)a.o;
+  if (a.causal)
+    hipLaunchKernelGGL((prefill16_skew_kernel<TT, D, true>), grid, dim3(512), 0, st, q, k, v, o, a.lse,
+                       a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
+  else
+    hipLaunchKernelGGL((prefill16_skew_kernel<TT, D, false>), grid, dim3(512), 0, st, q, k, v, o, a.lse,
+                       a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
+  return hipGetLastError();
+}
+
 template <class TT, int D>
 hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
   const char* env = getenv("ATTN_PREFILL_VARIANT");
@@ -1561,6 +1799,7 @@ hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
   if (variant == 6) return launch16w2<TT, D>(a, st);
   if (variant == 7) return launch16q<TT, D, 1, 8>(a, st);
   if (variant == 8) return launch16q<TT, D, 1, (D == 128 ? 8 : 4)>(a, st);
+  if (variant == 9) return launch16skew<TT, D>(a, st);
   return launch16pers<TT, D, (D == 128 ? 8 : 4)>(a, st);
 }
 

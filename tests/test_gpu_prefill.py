@@ -173,7 +173,7 @@ def test_prefill_persistent_grid_many_items(shape, causal, slots, monkeypatch):
     _run_small(*shape, "bf16", causal, seed=zlib.crc32(repr((shape, causal)).encode()) % 10000)
 
 
-@pytest.mark.parametrize("variant", ["1", "2", "3", "4", "5", "6", "7", "8"])
+@pytest.mark.parametrize("variant", ["1", "2", "3", "4", "5", "6", "7", "8", "9"])
 def test_prefill_variants_match_oracle(variant, monkeypatch):
     """Every alternative kernel behind ATTN_PREFILL_VARIANT (tuning only) meets
     the same bar as the default."""
