@@ -251,6 +251,16 @@ def bench_backward(cfg, steps, warmup, torch, E):
             "wall_s": wall}
 
 
+def library_gemm_tflops(torch, n=8192, steps=20):
+    """A plain bf16 GEMM through torch (hipBLASLt) on this GPU: the practical
+    matrix-core rate under the card's power limit, reported beside the nominal peak."""
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    ms, _ = time_launches(lambda: torch.matmul(a, b), steps, 30, torch)
+    del a, b
+    return 2 * n ** 3 / (ms * 1e-3) / 1e12
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=3):
     """A plain device-to-device copy of known size (torch's copy kernel): the
     HBM counters read for it calibrate the FETCH_SIZE / WRITE_SIZE scale."""
@@ -351,6 +361,9 @@ def main(argv=None):
         res["prefill"] = bench_prefill(A.CONFIGS[2], args.steps, args.warmup, torch, E)
         print(f"# prefill c2: {res['prefill']['ms']:.3f} ms  {res['prefill']['tflops']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
+    if args.only in (None, "prefill"):
+        res["gemm"] = library_gemm_tflops(torch)
+        print(f"# bf16 8192^3 GEMM (torch/hipBLASLt): {res['gemm']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     if args.only in (None, "backward"):
         r = bench_backward(A.CONFIGS[2], args.steps, args.warmup, torch, E)
         print(f"# backward c2: {r['ms']:.3f} ms  {r['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
@@ -427,8 +440,11 @@ def main(argv=None):
         line["roofline"] = {"bound": "mfma", "achieved": round(p["tflops"], 3), "peak": PEAK_MFMA_16BIT,
                             "unit": "TFLOP/s", "frac": round(p["tflops"] / PEAK_MFMA_16BIT, 4),
                             "traffic": measured_traffic("prefill"),
-                            "kernel": "prefill16_kernel<BF16,128,causal>",
+                            "kernel": "prefill16_kernel<BF16,128,causal> (persistent grid)",
                             "work_per_launch": p["flops"]}
+        if "gemm" in res:
+            line["roofline"]["library_gemm_tflops"] = round(res["gemm"], 1)
+            line["roofline"]["frac_of_library_gemm"] = round(p["tflops"] / res["gemm"], 4)
     if d:
         line["decode"] = {"workload": "GQA decode, bf16, B=64, H_q=32, H_kv=4 (G=8), d=128, "
                                       "KV 32768 per request", "ms_per_step": round(d["ms"], 5),
