@@ -108,27 +108,14 @@ __device__ __forceinline__ void buffer_store8(__amdgpu_buffer_rsrc_t r, uint32_t
   __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)byte_off, 0, 0);
 }
 
-// 16-byte load from a raw buffer straight into LDS: lane j's 16 bytes land at
-// lds_base + 16*j (lds_base is wavefront-uniform, set in M0 within the same
-// asm block). Out-of-range offsets read zeros. The instruction has no
-// destination register; its completion is tracked by the caller with
-// s_waitcnt vmcnt (the compiler does not count it), and nothing else in the
-// calling loop may rely on compiler-inserted vmcnt waits.
-typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4_t raw_rsrc(const void* base, uint32_t nbytes) {
-  const uint64_t a = (uint64_t)base;
-  i32x4_t r;
-  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32) & 0xffff);
-  r[2] = __builtin_amdgcn_readfirstlane((int32_t)nbytes);
-  r[3] = 0x00020000;
-  return r;
-}
-__device__ __forceinline__ void dma_load16(i32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(lds_base)
-               : "memory", "m0");
+// 16-byte load from a raw buffer straight into LDS (buffer_load_dwordx4 ...
+// lds): lane j's 16 bytes land at lds_addr + 16*j, where lds_addr (a byte
+// address in LDS) is wavefront-uniform. Out-of-range offsets read zeros. The
+// compiler tracks the load like any other, so reads of that LDS region wait
+// for it.
+__device__ __forceinline__ void dma_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_addr) {
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(uintptr_t)lds_addr, 16, (int)voff, 0, 0, 0);
 }
 
 // LDS transposing read (gfx950 ds_read_b64_tr_b16). Within each group of 16

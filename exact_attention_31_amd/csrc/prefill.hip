@@ -1160,8 +1160,8 @@ __global__ __launch_bounds__(kThreads, (D == 128 ? 2 : 4)) void prefill16_dl_ker
     kg_off[i] = (uint32_t)(r * L::RB + ((slot ^ L::kswz(r)) * 16));
     vg_off[i] = (uint32_t)(r * L::RB + ((slot ^ L::vswz(r)) * 16));
   }
-  const i32x4_t dK = raw_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-  const i32x4_t dV = raw_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
+  const auto dK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
+  const auto dV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   auto issue_tile = [&](int t) {
     const int stage = t % kDLStages;
@@ -1341,8 +1341,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill16_w2_kernel(
     kg_off[i] = (uint32_t)(r * L::RB + ((slot ^ L::kswz(r)) * 16));
     vg_off[i] = (uint32_t)(r * L::RB + ((slot ^ L::vswz(r)) * 16));
   }
-  const i32x4_t dK = raw_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-  const i32x4_t dV = raw_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
+  const auto dK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
+  const auto dV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   auto issue_tile = [&](int t) {
     const int stage = t & (kW2Stages - 1);
