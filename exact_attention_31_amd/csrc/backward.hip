@@ -11,9 +11,10 @@
 //
 // Three kernels, no atomics (deterministic):
 //   bwd_prep_kernel   Delta and the log-sum-exp in log2 units, per query row;
-//   bwd_dkdv_kernel   one workgroup per 128 keys of a KV head; each wavefront
-//                     keeps 32 keys of K and V in registers and accumulates
-//                     dK^T, dV^T while Q and dO tiles stream through LDS;
+//   bwd_dkdv_kernel   one workgroup per 256 keys of a KV head; each wavefront
+//                     keeps 32 keys of K in registers (their V rows in LDS)
+//                     and accumulates dK^T, dV^T while Q and dO tiles stream
+//                     through LDS;
 //   bwd_dq_kernel     one workgroup per 32*NW query rows; each wavefront keeps
 //                     its Q and dO rows in registers and accumulates dQ^T while
 //                     K and V tiles stream through LDS.
@@ -30,7 +31,8 @@ namespace {
 
 constexpr int kBwdBM = 64;   // query rows per LDS tile (dK/dV kernel)
 constexpr int kBwdBN = 64;   // keys per LDS tile (dQ kernel)
-constexpr int kBwdKW = 128;  // keys per workgroup (dK/dV kernel): 4 wavefronts x 32
+constexpr int kBwdNWK = 8;   // wavefronts per dK/dV workgroup (two per SIMD)
+constexpr int kBwdKW = 32 * kBwdNWK;  // keys per dK/dV workgroup
 
 template <int D> struct BwdLds {
   static constexpr int STR = D + 8;  // row stride (elements) of staged Q, dO, K, V rows
@@ -104,17 +106,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV. Workgroup: 128 keys [k0, k0+128) of KV head hk of batch b; wavefront
-// w owns keys kw = k0 + 32w .. kw + 31 (lane: key kw + lane % 32 as the B
-// operand column of S = Q K^T and dP = dO V^T). Query tiles of 64 rows of each
-// of the G query heads stream through LDS (double-buffered, register-staged).
-// Per 32-row subtile:
-//   S  = Q K^T, dP = dO V^T           (A: Q, dO rows from LDS; B: K, V in registers)
+// dK, dV. Workgroup: 256 keys [k0, k0+256) of KV head hk of batch b, eight
+// wavefronts (two per SIMD); wavefront w owns keys kw = k0 + 32w .. kw + 31
+// (lane: key kw + lane % 32 as the B operand column of S = Q K^T and
+// dP = dO V^T). The K operands stay in registers; the V operands are read from
+// an LDS copy of the workgroup's V rows, which keeps the register count at two
+// wavefronts per SIMD. Query tiles of 64 rows of each of the G query heads
+// stream through LDS (double-buffered, register-staged). Per 32-row subtile:
+//   S  = Q K^T, dP = dO V^T           (A: Q, dO rows from LDS; B: K in registers, V from LDS)
 //   P  = exp2(S * scale*log2e - lse2), dS = P o (dP - Delta)   (per element)
 //   dV^T += dO^T P,  dK^T += Q^T dS   (A: dO^T, Q^T by transposing LDS reads;
 //                                      B: P, dS straight from the accumulators)
 template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int H_q, int H_kv, int N_q, int N_kv,
@@ -123,13 +127,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   constexpr int KS = D / 16;   // k-steps over the head dimension
   constexpr int DB = D / 32;   // 32-wide blocks of the head dimension
   constexpr int CPR = D / 8;   // 16-byte chunks per row
-  constexpr int NT = 256;
+  constexpr int NT = 64 * kBwdNWK;
   constexpr int LPT = kBwdBM * CPR / NT;  // 16-byte loads per thread per tile, per tensor
   static_assert(LPT * NT == kBwdBM * CPR, "tile load must split evenly");
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kBwdBM * STR];
   __shared__ __attribute__((aligned(16))) uint16_t sG[2][kBwdBM * STR];
   __shared__ __attribute__((aligned(16))) float sL[2][kBwdBM];
   __shared__ __attribute__((aligned(16))) float sD[2][kBwdBM];
+  __shared__ __attribute__((aligned(16))) uint16_t sVk[kBwdKW * STR];  // this workgroup's V rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -150,13 +155,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const auto rK = buffer_rsrc(K + kv_head, head_kv_bytes);
   const auto rV = buffer_rsrc(V + kv_head, head_kv_bytes);
 
-  // K and V as B operands: lane holds key kw + lr, d = 16*st + 8*lh + 0..7
-  u32x4_t kB[KS], vB[KS];
+  // K as B operands: lane holds key kw + lr, d = 16*st + 8*lh + 0..7
+  u32x4_t kB[KS];
 #pragma unroll
-  for (int st = 0; st < KS; ++st) {
+  for (int st = 0; st < KS; ++st)
     kB[st] = buffer_load16(rK, (uint32_t)((kw + lr) * D + 16 * st + 8 * lh) * 2);
-    vB[st] = buffer_load16(rV, (uint32_t)((kw + lr) * D + 16 * st + 8 * lh) * 2);
+  // the workgroup's V rows into LDS (visible after the first barrier below);
+  // the V operand of lane (key kw + lr, k-step st) is at vrow + 16*st
+  {
+    constexpr int VC = kBwdKW * CPR / NT;
+    static_assert(VC * NT == kBwdKW * CPR, "V rows must split evenly");
+#pragma unroll
+    for (int i = 0; i < VC; ++i) {
+      const int c = tid + NT * i;
+      const u32x4_t x = buffer_load16(rV, (uint32_t)((k0 + c / CPR) * D + (c % CPR) * 8) * 2);
+      *(u32x4_t*)(&sVk[(c / CPR) * STR + (c % CPR) * 8]) = x;
+    }
   }
+  const uint16_t* vrow = &sVk[(32 * wave + lr) * STR + 8 * lh];
 
   // query tiles: the G heads in turn, each from the first tile that sees key k0
   const int nqt = (N_q + kBwdBM - 1) / kBwdBM;
@@ -238,7 +254,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         const u32x4_t aq = *(const u32x4_t*)(tq + a_lane + 16 * st);
         const u32x4_t ag = *(const u32x4_t*)(tg + a_lane + 16 * st);
         s = TT::mfma32(aq, kB[st], s);
-        dp = TT::mfma32(ag, vB[st], dp);
+        dp = TT::mfma32(ag, *(const u32x4_t*)(vrow + 16 * st), dp);
       }
       // rows of accumulator r: query qs + 8*(r/4) + 4*lh + r%4; column: key kw + lr
       const bool need_mask = CAUSAL && (kw + 31 > qs + off);
@@ -487,12 +503,12 @@ hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
     const int nkb = (a.N_kv + kBwdKW - 1) / kBwdKW;
     const unsigned g = xcd_grid((int64_t)nkb * a.H_kv * a.B);
     if (a.causal)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, true>), dim3(g), dim3(256), 0, st,
+      hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, true>), dim3(g), dim3(64 * kBwdNWK), 0, st,
                          (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                          (const uint16_t*)a.d_o, a.lse2, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
                          a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, a.scale, nkb, a.B);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, false>), dim3(g), dim3(256), 0, st,
+      hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, false>), dim3(g), dim3(64 * kBwdNWK), 0, st,
                          (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                          (const uint16_t*)a.d_o, a.lse2, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
                          a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, a.scale, nkb, a.B);
