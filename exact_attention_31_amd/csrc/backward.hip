@@ -15,7 +15,7 @@
 //                     keeps 32 keys of K in registers (their V rows in LDS)
 //                     and accumulates dK^T, dV^T while Q and dO tiles stream
 //                     through LDS;
-//   bwd_dq_kernel     one workgroup per 32*NW query rows; each wavefront keeps
+//   bwd_dq_kernel     one workgroup per 256 query rows; each wavefront keeps
 //                     its Q and dO rows in registers and accumulates dQ^T while
 //                     K and V tiles stream through LDS.
 // Matrix-core layouts are those of the forward kernels (32x32x16 MFMA); the
@@ -321,8 +321,8 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ. Two resident workgroups per compute unit (registers capped so that two
-// wavefronts share each SIMD). Workgroup: 32*NW query rows of head h of batch b; lane: query row
+// dQ. Two wavefronts per SIMD (registers capped accordingly). Workgroup:
+// 32*NW query rows of head h of batch b; lane: query row
 // q0 + lane % 32 as the B operand column of S^T = K Q^T and dP^T = V dO^T.
 // Key tiles of 64 rows stream through LDS (double-buffered, register-staged).
 // Per 32-key half:
@@ -516,7 +516,7 @@ hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (a.N_q > 0) {
-    constexpr int NW = 4;
+    constexpr int NW = 8;  // 256 rows per workgroup, two wavefronts per SIMD
     const int nqb = (a.N_q + 32 * NW - 1) / (32 * NW);
     const unsigned g = xcd_grid((int64_t)nqb * a.H_q * a.B);
     if (a.causal)

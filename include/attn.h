@@ -197,7 +197,7 @@ size_t attn_backward_workspace_size(int B, int H_q, int H_kv, int N_q, int N_kv,
  * dq, dk, dv are written in full (no accumulation into them); they must not
  * overlap any input, each other or the workspace. Three kernels run on
  * `stream`: per-row Delta, then dK/dV (one workgroup per 256 keys), then dQ
- * (one workgroup per 128 query rows); no atomics, so results are
+ * (one workgroup per 256 query rows); no atomics, so results are
  * deterministic.
  * Work: 10*d FLOP per visible (query, key) pair per query head in the five
  * products (the recomputation adds 4*d more).
