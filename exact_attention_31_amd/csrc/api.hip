@@ -1,6 +1,7 @@
 // C-ABI entry points: argument checks, device checks, dispatch to the kernels.
 // Nothing is enqueued unless every check passes; no allocation, no sync.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -190,6 +191,26 @@ int decode_launch(const void* q, const void* k, const void* v, size_t kv_bytes, 
   float* ws = (float*)workspace;
   int dev = 0;
   (void)hipGetDevice(&dev);
+  // Many query rows per KV head (G * N_q, several new tokens) and enough
+  // of them to fill the device: the rows are a tall product, better served by
+  // the prefill kernel in rows mode (32x32 MFMA tiles, K/V shared through LDS)
+  // than by the split-KV decode kernel. ATTN_DECODE_ROWS_MODE = 0 / 1 forces it
+  // off / on (contiguous 16-bit caches only).
+  if (!paged && !kv_fp8) {
+    const int rows = (H_q / H_kv) * N_q;
+    const int bm = d == 128 ? 256 : 128;  // query rows per prefill workgroup
+    const int64_t items = (int64_t)B * H_kv * ((rows + bm - 1) / bm);
+    // at least half a workgroup's rows (padding rows cost as much as real ones)
+    bool rows_mode = 2 * rows >= bm && items >= (g_dev_cus[dev] > 0 ? g_dev_cus[dev] : 256);
+    if (const char* e = getenv("ATTN_DECODE_ROWS_MODE")) rows_mode = atoi(e) != 0;
+    if (rows_mode) {
+      attn::PrefillArgs pa{q, k, v, o, lse, B, H_kv, H_kv, rows, N_kv, d, causal, scale, dtype,
+                           g_dev_cus[dev]};
+      return attn::launch_prefill_rows(pa, kv_lens, N_q, (hipStream_t)stream) == hipSuccess
+                 ? ATTN_OK
+                 : ATTN_ERR_LAUNCH;
+    }
+  }
   attn::DecodeArgs a{q, k, v, kv_lens, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale, dtype,
                      plan.chunk, plan.splits, g_dev_cus[dev], ws,
                      ws + (size_t)B * H_q * N_q * plan.splits * d,

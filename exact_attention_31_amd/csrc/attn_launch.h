@@ -79,6 +79,10 @@ struct BackwardArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// Prefill kernel in rows mode: a.N_q rows per "head" are row_period tokens of
+// a.N_q / row_period query heads; kv_lens (nullable) bounds each request's keys.
+hipError_t launch_prefill_rows(const PrefillArgs& a, const int* kv_lens, int row_period,
+                               hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -87,11 +87,16 @@ template <int QB, int D> struct Occ {
   static constexpr int kWaves = (QB == 2 && D == 128) ? 1 : 2;  // wavefronts per SIMD
 };
 
+// Rows mode (row_period P > 0, used by multi-token decode): the N_q rows of a
+// "head" are P consecutive tokens of each of N_q / P query heads that share
+// one KV head, row r being token r % P; causal alignment is per token, and
+// kv_lens (if given) bounds each request's keys.
 template <class TT, int D, bool CAUSAL, int QB, int NW = 4, bool PERSIST = false>
 __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void prefill16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
-    float scale_log2, int nqb, int nbatch) {
+    float scale_log2, int nqb, int nbatch, const int* __restrict__ kv_lens = nullptr,
+    int row_period = 0) {
   constexpr int KST = Lds16<D>::kK;
   constexpr int VST = Lds16<D>::kV;
   constexpr int KS = D / 16;   // k-steps of the score MFMA
@@ -110,9 +115,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int off = N_kv - N_q;  // bottom-right causal alignment
   const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
-  const uint32_t head_kv_bytes = (uint32_t)N_kv * D * 2;
 
   // ---- work items. One per workgroup (map_work), or, persistent: the grid
   // holds as many workgroups as can be resident, and each walks items of its
@@ -147,6 +150,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
   struct Ctx {
     __amdgpu_buffer_rsrc_t rQ, rK, rV;
     int b, h, qblk, q0, ntiles;
+    int lo_lim, hi_lim;  // least and greatest key limit over the wavefront's rows
     int qrow[QB], lim[QB];
   };
   auto ctx_of = [&](const WorkItem& wi) {
@@ -155,20 +159,34 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
     c.h = wi.h;
     c.qblk = wi.qblk;
     const int hk = wi.h / (H_q / H_kv);
+    const int len = kv_lens ? min(max(kv_lens[wi.b], 0), N_kv) : N_kv;  // this request's keys
+    const int ntok = row_period > 0 ? row_period : N_q;  // query tokens per head
+    const int off = len - ntok;                          // bottom-right causal alignment
     c.rQ = buffer_rsrc(Q + ((int64_t)wi.b * H_q + wi.h) * (int64_t)N_q * D, head_q_bytes);
-    c.rK = buffer_rsrc(K + ((int64_t)wi.b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-    c.rV = buffer_rsrc(V + ((int64_t)wi.b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
+    c.rK = buffer_rsrc(K + ((int64_t)wi.b * H_kv + hk) * (int64_t)N_kv * D, (uint32_t)len * D * 2);
+    c.rV = buffer_rsrc(V + ((int64_t)wi.b * H_kv + hk) * (int64_t)N_kv * D, (uint32_t)len * D * 2);
     c.q0 = wi.qblk * BM + wave * 32 * QB;  // first row of this wavefront
+    int lo = len, hi = 0;
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       c.qrow[j] = c.q0 + 32 * j + lr;  // this lane's row in query block j
+      const int tok = row_period > 0 ? c.qrow[j] % row_period : c.qrow[j];
       // keys below lim[j] are visible to that row
-      c.lim[j] = CAUSAL ? min(N_kv, max(c.qrow[j] + off + 1, 0)) : N_kv;
+      c.lim[j] = CAUSAL ? min(len, max(tok + off + 1, 0)) : len;
+      lo = min(lo, c.lim[j]);
+      hi = max(hi, c.lim[j]);
     }
-    int kv_end = N_kv;
-    if (CAUSAL) {
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+      lo = min(lo, __shfl_xor(lo, o));
+      hi = max(hi, __shfl_xor(hi, o));
+    }
+    c.lo_lim = __builtin_amdgcn_readfirstlane(lo);
+    c.hi_lim = __builtin_amdgcn_readfirstlane(hi);
+    int kv_end = len;
+    if (CAUSAL && row_period == 0) {
       const int qlast = min(wi.qblk * BM + BM - 1, N_q - 1);
-      kv_end = min(N_kv, qlast + off + 1);
+      kv_end = min(len, qlast + off + 1);
     }
     c.ntiles = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
     return c;
@@ -249,7 +267,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
       m[j] = kNegInf;  // reference maximum, in units of log2 (scores * scale * log2 e)
       l[j] = 0.f;      // this half-wave's part of the denominator
     }
-    const int ntiles = c.ntiles, q0 = c.q0;
+    const int ntiles = c.ntiles;
 
     for (int t = 0; t < ntiles; ++t) {
       const int buf = (t + par) & 1;
@@ -258,7 +276,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
       else if (has_next) load_tile(cn, 0);
       const int kv0 = t * kBN;
       // wavefront-uniform: does this tile hold any key visible to this wavefront?
-      const bool live = !CAUSAL || kv0 <= q0 + 32 * QB - 1 + off;
+      const bool live = kv0 < c.hi_lim;
       if (live) {
         const uint16_t* tK = &sK[0][0] + buf * (kBN * KST) + k_lane;
         const uint16_t* tV = &sV[0][0] + buf * (kBN * VST) + v_lane;
@@ -296,7 +314,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
             vop[t4][db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
           }
         // ---- mask (tail and causal diagonal tiles only), branch-free per element
-        const bool need_mask = (kv0 + kBN > N_kv) || (CAUSAL && kv0 + kBN - 1 > q0 + off);
+        const bool need_mask = kv0 + kBN > c.lo_lim;
         if (need_mask) {
 #pragma unroll
           for (int j = 0; j < QB; ++j) {
@@ -1632,7 +1650,8 @@ inline int xcd_grid(int64_t items) { return (int)(((items + 7) / 8) * 8); }
 // causal items of very different lengths, and the hardware's dynamic dispatch
 // of one item per workgroup does better; the persistent grid is used above that.
 template <class TT, int D, int NW, bool CAUSAL>
-hipError_t launch16pers_t(const PrefillArgs& a, hipStream_t st, int nqb) {
+hipError_t launch16pers_t(const PrefillArgs& a, hipStream_t st, int nqb, const int* kv_lens = nullptr,
+                          int row_period = 0) {
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
@@ -1652,21 +1671,22 @@ hipError_t launch16pers_t(const PrefillArgs& a, hipStream_t st, int nqb) {
     hipLaunchKernelGGL((prefill16_kernel<TT, D, CAUSAL, 1, NW, false>), dim3(xcd_grid(items)),
                        dim3(64 * NW), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2,
-                       nqb, a.B);
+                       nqb, a.B, kv_lens, row_period);
   } else {
     hipLaunchKernelGGL((prefill16_kernel<TT, D, CAUSAL, 1, NW, true>), dim3(xcd_grid(slots)),
                        dim3(64 * NW), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2,
-                       nqb, a.B);
+                       nqb, a.B, kv_lens, row_period);
   }
   return hipGetLastError();
 }
 
 template <class TT, int D, int NW>
-hipError_t launch16pers(const PrefillArgs& a, hipStream_t st) {
+hipError_t launch16pers(const PrefillArgs& a, hipStream_t st, const int* kv_lens = nullptr,
+                        int row_period = 0) {
   const int nqb = (a.N_q + NW * 32 - 1) / (NW * 32);
-  return a.causal ? launch16pers_t<TT, D, NW, true>(a, st, nqb)
-                  : launch16pers_t<TT, D, NW, false>(a, st, nqb);
+  return a.causal ? launch16pers_t<TT, D, NW, true>(a, st, nqb, kv_lens, row_period)
+                  : launch16pers_t<TT, D, NW, false>(a, st, nqb, kv_lens, row_period);
 }
 
 template <class TT, int D, int QB, int NW = 4>
@@ -1822,6 +1842,17 @@ hipError_t launch32(const PrefillArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+// The default kernel in rows mode (multi-token decode against per-request
+// lengths; see prefill16_kernel).
+hipError_t launch_prefill_rows(const PrefillArgs& a, const int* kv_lens, int row_period,
+                               hipStream_t st) {
+  if (a.dtype == kDtypeBF16)
+    return a.d == 64 ? launch16pers<BF16, 64, 4>(a, st, kv_lens, row_period)
+                     : launch16pers<BF16, 128, 8>(a, st, kv_lens, row_period);
+  return a.d == 64 ? launch16pers<F16, 64, 4>(a, st, kv_lens, row_period)
+                   : launch16pers<F16, 128, 8>(a, st, kv_lens, row_period);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   switch (a.dtype) {

@@ -170,3 +170,22 @@ def test_decode_column_groups_per_wavefront_agree(groups, monkeypatch):
     monkeypatch.setenv("ATTN_DECODE_GROUPS", groups)
     _decode_case(2, 16, 2, 2100, 128, "bf16", [2100, 999], seed=93, Nq=6, causal=True)
     _decode_case(2, 8, 2, 1100, 64, "f16", [1100, 64], seed=94, Nq=3, causal=True)
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", MULTI, ids=lambda c: "x".join(map(str, c[:6])))
+def test_decode_rows_mode_matches_oracle(case, dtype, causal, monkeypatch):
+    """Multi-token decode through the prefill kernel in rows mode (forced here;
+    chosen automatically for many rows per KV head and many KV heads)."""
+    monkeypatch.setenv("ATTN_DECODE_ROWS_MODE", "1")
+    B, Hq, Hkv, Nkv, d, Nq, lens = case
+    _decode_case(B, Hq, Hkv, Nkv, d, dtype, lens,
+                 seed=zlib.crc32(repr((case, dtype, causal, "rows")).encode()) % 10000, Nq=Nq,
+                 causal=causal)
+
+
+def test_decode_rows_mode_chosen_for_tall_batches():
+    """64 requests x 4 KV heads x (8 heads x 16 tokens) rows: rows mode by default."""
+    lens = np.random.default_rng(3).integers(1, 2001, size=64).astype(np.int32)
+    _decode_case(64, 32, 4, 2000, 128, "bf16", lens, seed=95, Nq=16, causal=True)
