@@ -4,9 +4,9 @@ Shapes follow the pages' workloads: a 512-step single head; causal MHA
 prefill at 4096; a one-day-at-1-second causal series (23,400 steps, 12 heads);
 causal GQA prefill at ISL 32768 with group size 8; GQA decode against a
 32768-token KV cache for 64 requests (uniform or ragged lengths); and the
-same decode with 4 new tokens per request (speculative decoding makes the
-decode product taller, which the pages name as the way decode moves toward
-compute).
+same decode with 4 or 64 new tokens per request (speculative decoding and
+prefix caching make the decode product taller, which the pages name as the
+way decode moves toward compute).
 """
 from dataclasses import dataclass, field
 import math
@@ -60,6 +60,9 @@ CONFIGS = {
     # 5's, the queries are 4 per request and head, causally aligned at the end
     7: Config(5, "GQA multi-token decode bf16 (4 tokens per request)", "decode", "bf16", 64, 32, 4, 4,
               32768, 128, True, 1.0),
+    # 64 new tokens per request (chunked prefill against the cache): compute-bound
+    8: Config(5, "GQA multi-token decode bf16 (64 tokens per request)", "decode", "bf16", 64, 32, 4,
+              64, 32768, 128, True, 1.0),
 }
 
 

@@ -10,7 +10,8 @@ Default run (one JSON line on stdout):
   * "roofline" relates the prefill kernel's rate (from HIP events on its launch
     stream) to the bf16 MFMA peak; "decode_roofline" relates decode to HBM peak;
   * "decode_multi_token" times the same caches with 4 new tokens per request
-    (causal, bottom-right aligned), as a speculative-decoding verifier sees it;
+    (causal, bottom-right aligned), as a speculative-decoding verifier sees it,
+    and "decode_multi_token_64" with 64 (compute-bound, in TFLOP/s);
   * "decode_paged" times the same caches cut into 16-position blocks scattered
     over a pool and read through a block table;
   * "decode_fp8" times the same caches stored as FP8 E4M3 codes (half the bytes);
@@ -380,6 +381,10 @@ def main(argv=None):
         res["decode_multi"] = r
         if args.only == "decode_multi":
             res["decode"] = r
+        r, cache = bench_decode(A.CONFIGS[8], args.steps, args.warmup, torch, E, cache=cache)
+        print(f"# decode c5, 64 tokens: {r['ms']:.3f} ms  {r['gb_per_s']:.0f} GB/s  "
+              f"{r['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        res["decode_multi64"] = r
     if args.only in (None, "decode_paged"):
         if cache is None:
             _, cache = bench_decode(A.CONFIGS[5], 1, 1, torch, E)
@@ -463,6 +468,15 @@ def main(argv=None):
             "ms_per_step": round(dm["ms"], 5), "value": round(dm["gb_per_s"], 2), "unit": "GB/s",
             "frac_of_hbm_peak": round(dm["frac_of_peak"], 4), "tflops": round(dm["tflops"], 2),
             "kernel": "decode_split_kernel + decode_merge_kernel (one step)"}
+    dm64 = res.get("decode_multi64")
+    if dm64:
+        line["decode_multi_token_64"] = {
+            "workload": "GQA multi-token decode, bf16, B=64, 64 new tokens per request (causal, "
+                        "bottom-right), H_q=32, H_kv=4 (G=8), d=128, KV 32768 per request",
+            "ms_per_step": round(dm64["ms"], 5), "value": round(dm64["tflops"], 2), "unit": "TFLOP/s",
+            "frac_of_mfma_peak": round(dm64["tflops"] / PEAK_MFMA_16BIT, 4),
+            "kv_gb_per_s": round(dm64["gb_per_s"], 2),
+            "kernel": "prefill16_kernel in rows mode (one step)"}
     dp = res.get("decode_paged")
     if dp and dp is not d:
         line["decode_paged"] = {

@@ -43,3 +43,4 @@ def test_config_table():
     np.testing.assert_array_equal(lens, A.ragged_lengths(c[6]))
     # multi-token decode shares config 5's caches (same seeds), 4 queries per head
     assert (c[7].cid, c[7].N_q, c[7].N_kv, c[7].causal, c[7].G) == (5, 4, 32768, True, 8)
+    assert (c[8].cid, c[8].N_q, c[8].N_kv, c[8].causal) == (5, 64, 32768, True)
