@@ -12,13 +12,16 @@
 // statistics never cross wavefronts (FA2's third change). Key blocks that lie
 // entirely after a causal query block are never loaded (causal skipping).
 //
-// gfx950 mapping (one workgroup = 4 wavefronts = 128 query rows):
+// gfx950 mapping (one workgroup = NW wavefronts of 32 query rows: 8 for
+// d = 128, 4 for d = 64; a persistent grid when work items are plentiful):
 //   * Q rows stay in VGPRs for the whole loop, laid out as the B operand of
 //     S^T = K Q^T (v_mfma_f32_32x32x16): each lane owns one query row, and the
 //     accumulator layout then gives each lane 16 of the 32 scores of its row,
 //     so the row max/sum needs one exchange with the opposite half-wave only.
-//   * K and V tiles (64 keys) are staged through LDS with 16-byte coalesced
-//     loads; all four wavefronts read them.
+//   * K and V tiles (64 keys) go through LDS, shared by all the workgroup's
+//     wavefronts: staged through registers with 16-byte coalesced loads
+//     (prefill16_kernel), or streamed by direct-to-LDS loads into a ring
+//     (prefill16_ring_kernel).
 //   * The probabilities, rounded to the input type, are reused in registers as
 //     the B operand of O^T = V^T P^T; V^T comes from LDS through the gfx950
 //     transposing read, so each lane's output accumulators belong to its own
@@ -66,7 +69,7 @@ constexpr float kLazyRescale = 8.f;
 // reuse its L2, while every XCD gets the same number of items.
 struct WorkItem {
   int b, h, qblk;
-  bool valid;
+  int valid;  // an int, not a bool: no padding bytes for a struct copy to move
 };
 __device__ __forceinline__ WorkItem map_work(int nqb, int H_q, int B, bool longest_first) {
   const int id = blockIdx.x;
@@ -84,7 +87,8 @@ __device__ __forceinline__ WorkItem map_work(int nqb, int H_q, int B, bool longe
 }
 
 template <int QB, int D> struct Occ {
-  static constexpr int kWaves = (QB == 2 && D == 128) ? 1 : 2;  // wavefronts per SIMD
+  // wavefronts per SIMD the register budget must allow (d = 64 fits three)
+  static constexpr int kWaves = (QB == 2 && D == 128) ? 1 : (QB == 1 && D == 64) ? 3 : 2;
 };
 
 // Rows mode (row_period P > 0, used by multi-token decode): the N_q rows of a
@@ -237,9 +241,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
     }
   };
 
-  WorkItem first;
-  if (!next_item(first)) return;
-  Ctx c = ctx_of(first);
+  WorkItem cur;
+  if (!next_item(cur)) return;
+  Ctx c = ctx_of(cur);
   // Tile 0 is staged unconditionally (loads past the end read zeros): with no
   // branch here every load issued so far has completed when the loop starts,
   // so the loop only ever waits for its own prefetch, at the LDS store.
@@ -254,9 +258,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
     // The next item's tile 0 is loaded during this item's last tile, and its
     // Q rows at the end of that tile, so that the next item starts with its
     // operands in place.
-    WorkItem nwi;
+    // (with no next item, nwi stays the current one and cn is not used)
+    WorkItem nwi = cur;
     const bool has_next = next_item(nwi);
-    const Ctx cn = has_next ? ctx_of(nwi) : c;
+    const Ctx cn = ctx_of(nwi);
 
     f32x16_t oacc[QB][DB];
     float m[QB], l[QB];
@@ -413,7 +418,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
     vmem_wait_all();
     __syncthreads();
     par = (par + (ntiles > 0 ? ntiles : 1)) & 1;
-    c = cn;
+    cur = nwi;
+    c = ctx_of(cur);
   }
 }
 
@@ -1114,11 +1120,11 @@ __global__ __launch_bounds__(kPPThreads, 1) void prefill16_pp_kernel(
 constexpr int kDLBN = 32;
 constexpr int kDLStages = 3;
 
-template <int D> struct DL {
+template <int D, int BN = kDLBN> struct DL {
   static constexpr int RB = D * 2;
   static constexpr int CPR = D / 8;
   static constexpr int RPB = 256 / RB;
-  static constexpr int TILE = kDLBN * RB;       // bytes per tensor tile
+  static constexpr int TILE = BN * RB;          // bytes per tensor tile
   static constexpr int STAGE = 2 * TILE;        // K then V
   static constexpr int BLK = TILE / 1024;       // 1 KB load blocks per tensor tile
   static constexpr int BPW = BLK / 4;           // per wavefront
@@ -1526,6 +1532,346 @@ __global__ __launch_bounds__(kThreads, 1) void prefill16_w2_kernel(
   }
 }
 
+constexpr int kRingStages = 3;
+
+// Workgroup barrier for LDS hand-offs: this wavefront's LDS operations have
+// completed, and the compiler moves no memory access across it. Unlike
+// __syncthreads() it does not wait for outstanding global loads (a workgroup
+// release would, since direct-to-LDS loads count as LDS stores): each step
+// waits for exactly the loads it needs before calling it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Ring form of the default kernel. K and V tiles travel HBM -> LDS through
+// buffer loads that write LDS themselves (no staging registers and no LDS store
+// instructions) into a ring of three stages. The tiles of all the workgroup's
+// work items form one stream: while stream tile g is worked, the loads of tile
+// g+2 are issued, into the stage that tile g-1 used, so each tile has a whole
+// tile's time to arrive. They are issued after tile g's V operands have been
+// read: the compiler makes a transposing LDS read wait for every direct load in
+// flight, and at that point only tile g+1's loads are, which are due anyway.
+// LDS rows are unpadded, their 16-byte chunks XOR-swizzled as in the
+// direct-load form. One 32-row query block per wavefront; otherwise (work
+// items, masking, causal skipping, the online softmax) as the default kernel.
+template <class TT, int D, bool CAUSAL, int NW, bool PERSIST>
+__global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<1, D>::kWaves)) void prefill16_ring_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
+    float scale_log2, int nqb, int nbatch, const int* __restrict__ kv_lens = nullptr,
+    int row_period = 0) {
+  using L = DL<D, kBN>;
+  constexpr int KS = D / 16;   // k-steps of the score MFMA
+  constexpr int DB = D / 32;   // 32-wide blocks of the output
+  constexpr int BM = NW * 32;  // query rows per workgroup
+  constexpr int BPW = L::BLK / NW;  // 1 KB load blocks per wavefront, per tensor tile
+  static_assert(BPW >= 1 && BPW * NW == L::BLK, "tile loads must split over the wavefronts");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kRingStages * L::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
+
+  // work item r of this workgroup: as in the default kernel (a single item, or
+  // the zig-zag walk of a persistent slot over its XCD's range)
+  auto item_at = [&](int r, WorkItem& w) -> bool {
+    if constexpr (!PERSIST) {
+      if (r > 0) return false;
+      w = map_work(nqb, H_q, nbatch, CAUSAL);
+      return w.valid;
+    } else {
+      const int total = nqb * H_q * nbatch;
+      const int per_xcd = (total + 7) >> 3;
+      const int nslots = (int)gridDim.x >> 3, slot = (int)blockIdx.x >> 3;
+      const int it = r * nslots + ((r & 1) ? (nslots - 1 - slot) : slot);
+      const int item = (int)(blockIdx.x & 7) * per_xcd + it;
+      if (it >= per_xcd || item >= total) return false;
+      const int unit = item / nqb;
+      const int qi = item - unit * nqb;
+      w.valid = 1;
+      w.qblk = CAUSAL ? (nqb - 1 - qi) : qi;
+      w.b = unit / H_q;
+      w.h = unit - w.b * H_q;
+      return true;
+    }
+  };
+  // keys of the item's request, and the K/V tiles the item works
+  auto item_len = [&](const WorkItem& wi) {
+    return kv_lens ? min(max(kv_lens[wi.b], 0), N_kv) : N_kv;
+  };
+  auto item_tiles = [&](const WorkItem& wi, int len) {
+    int kv_end = len;
+    if (CAUSAL && row_period == 0) {
+      const int qlast = min(wi.qblk * BM + BM - 1, N_q - 1);
+      kv_end = min(len, qlast + (len - N_q) + 1);
+    }
+    return kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
+  };
+  auto kv_rsrc = [&](const uint16_t* base, const WorkItem& wi, int len) {
+    const int hk = wi.h / (H_q / H_kv);
+    return buffer_rsrc(base + ((int64_t)wi.b * H_kv + hk) * (int64_t)N_kv * D, (uint32_t)len * D * 2);
+  };
+
+  struct Ctx {
+    __amdgpu_buffer_rsrc_t rQ;
+    int b, h, ntiles;
+    int lo_lim, hi_lim;  // least and greatest key limit over the wavefront's rows
+    int qrow, lim;       // this lane's query row; keys below lim are visible to it
+  };
+  auto ctx_of = [&](const WorkItem& wi) {
+    Ctx c;
+    c.b = wi.b;
+    c.h = wi.h;
+    const int len = item_len(wi);
+    const int ntok = row_period > 0 ? row_period : N_q;  // query tokens per head
+    const int off = len - ntok;                          // bottom-right causal alignment
+    c.rQ = buffer_rsrc(Q + ((int64_t)wi.b * H_q + wi.h) * (int64_t)N_q * D, head_q_bytes);
+    c.qrow = wi.qblk * BM + wave * 32 + lr;
+    const int tok = row_period > 0 ? c.qrow % row_period : c.qrow;
+    c.lim = CAUSAL ? min(len, max(tok + off + 1, 0)) : len;
+    int lo = c.lim, hi = c.lim;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+      lo = min(lo, __shfl_xor(lo, o));
+      hi = max(hi, __shfl_xor(hi, o));
+    }
+    c.lo_lim = __builtin_amdgcn_readfirstlane(lo);
+    c.hi_lim = __builtin_amdgcn_readfirstlane(hi);
+    c.ntiles = item_tiles(wi, len);
+    return c;
+  };
+
+  // Q^T operand: lane holds row qrow, d = 16*s + 8*lh + 0..7 (rows past N_q read as 0)
+  u32x4_t qreg[KS];
+  auto load_q = [&](const Ctx& c) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qreg[s] = buffer_load16(c.rQ, (uint32_t)(c.qrow * D + 16 * s + 8 * lh) * 2);
+  };
+
+  // ---- the producer: direct loads of the stream's tiles, two ahead of the
+  // tile being worked. Block i of this wavefront fills LDS bytes
+  // [(wave*BPW + i) KB, +1 KB) of the tensor tile, lane j writing physical chunk
+  // p = 64*(wave*BPW + i) + j, which holds row p / CPR, logical chunk
+  // (p % CPR) ^ swizzle(row).
+  uint32_t kg_off[BPW], vg_off[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int p = (wave * BPW + i) * 64 + lane;
+    const int r = p / L::CPR, slot = p % L::CPR;
+    kg_off[i] = (uint32_t)(r * L::RB + ((slot ^ L::kswz(r)) * 16));
+    vg_off[i] = (uint32_t)(r * L::RB + ((slot ^ L::vswz(r)) * 16));
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  WorkItem pw;
+  int p_round = 0, p_t = 0, p_n = 0, p_stage = 0;
+  bool p_more = item_at(0, pw);
+  __amdgpu_buffer_rsrc_t pK, pV;
+  auto p_open = [&]() {  // the producer's current item
+    const int len = item_len(pw);
+    pK = kv_rsrc(K, pw, len);
+    pV = kv_rsrc(V, pw, len);
+    p_n = item_tiles(pw, len);
+    p_t = 0;
+  };
+  auto p_seek = [&]() {  // skip past exhausted items (and items without keys)
+    while (p_more && p_t >= p_n) {
+      p_more = item_at(++p_round, pw);
+      if (p_more) p_open();
+    }
+  };
+  if (p_more) p_open();
+  p_seek();
+  auto produce = [&]() -> bool {
+    if (!p_more) return false;
+    const uint32_t g0 = (uint32_t)(p_t * kBN) * L::RB;
+    const uint32_t sb = lds0 + p_stage * L::STAGE;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const uint32_t kd = sb + (wave * BPW + i) * 1024;
+      dma_load16(pK, g0 + kg_off[i], kd);
+      dma_load16(pV, g0 + vg_off[i], kd + L::TILE);
+    }
+    p_stage = (p_stage == kRingStages - 1) ? 0 : p_stage + 1;
+    ++p_t;
+    p_seek();
+    return true;
+  };
+
+  // operand addresses within a stage (bytes)
+  //   K (score A operand): row lr (+32 for the second key block), logical chunk 2*st + lh
+  //   V (transposing read): row 4*(g/2) + gi/4 (+16*t4, +8), logical chunk
+  //     4*db + 2*(g%2) + (gi%4)/2, 8-byte half gi%2 (g = lane/16, gi = lane%16)
+  int ka[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) ka[st] = lr * L::RB + (((2 * st + lh) ^ L::kswz(lr)) * 16);
+  const int g = lane >> 4, gi = lane & 15;
+  const int vrow = 4 * (g >> 1) + (gi >> 2);  // the swizzle only sees vrow % 4 (or % 8)
+  int va[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    va[db] = L::TILE + vrow * L::RB + (((4 * db + 2 * (g & 1) + ((gi & 3) >> 1)) ^ L::vswz(vrow)) * 16) +
+             8 * (gi & 1);
+
+  WorkItem cur;
+  if (!item_at(0, cur)) return;
+  Ctx c = ctx_of(cur);
+  int c_round = 0;
+  produce();
+  produce();
+  load_q(c);
+  vmem_wait_all();
+  __syncthreads();
+  int stage = 0;  // stage of the stream tile being worked
+
+  for (;;) {
+    WorkItem nwi = cur;  // (with no next item, nwi stays the current one, unused)
+    const bool has_next = item_at(c_round + 1, nwi);
+    const Ctx cn = ctx_of(nwi);
+
+    f32x16_t oacc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[i] = f32x16_t{0};
+    float m = kNegInf;  // reference maximum, in units of log2 (scores * scale * log2 e)
+    float l = 0.f;      // this half-wave's part of the denominator
+    const int ntiles = c.ntiles;
+
+    for (int t = 0; t < ntiles; ++t) {
+      const bool last = t + 1 == ntiles;
+      const uint8_t* sb = smem + stage * L::STAGE;
+      const int kv0 = t * kBN;
+      // wavefront-uniform: does this tile hold any key visible to this wavefront?
+      const bool live = kv0 < c.hi_lim;
+      f32x16_t s0, s1;
+      u32x4_t vop[4][DB];
+      if (live) {
+        // ---- S^T = K Q^T: two 32-key blocks
+        s0 = s1 = f32x16_t{0};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const u32x4_t a0 = *(const u32x4_t*)(sb + ka[st]);
+          const u32x4_t a1 = *(const u32x4_t*)(sb + ka[st] + 32 * L::RB);
+          s0 = TT::mfma32(a0, qreg[st], s0);
+          s1 = TT::mfma32(a1, qreg[st], s1);
+        }
+        // keep the K operand reads two k-steps ahead of the MFMAs that use them
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int st = 0; st < KS - 2; ++st) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        // V^T operands of this tile, requested now so that the score MFMAs, the
+        // row max and the exponentials cover their LDS latency
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const u32x2_t lo = lds_read_tr16((const uint16_t*)(sb + va[db] + 16 * t4 * L::RB));
+            const u32x2_t hi = lds_read_tr16((const uint16_t*)(sb + va[db] + (16 * t4 + 8) * L::RB));
+            vop[t4][db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          }
+      }
+      const bool issued = produce();
+      if (live) {
+        // ---- mask (tail and causal diagonal tiles only), branch-free per element
+        if (kv0 + kBN > c.lo_lim) {
+          // key kv0 + 4*lh + e (e a per-register constant) is visible iff e < rel
+          const int rel = c.lim - (kv0 + 4 * lh);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int e = 8 * (r >> 2) + (r & 3);
+            s0[r] = (e < rel) ? s0[r] : kNegInf;
+            s1[r] = (e + 32 < rel) ? s1[r] : kNegInf;
+          }
+        }
+        // ---- row max of the raw scores (scale > 0 commutes with max)
+        float mx = max3(s0[0], s0[1], s1[0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = max3(mx, s0[r], s1[r]);
+        mx = fmaxf(mx, s1[0]);
+        const float mxs = half_max(mx) * scale_log2;
+        // wavefront-uniform branch; each lane moves only its own reference
+        const bool need = mxs > m + kLazyRescale;
+        if (wave_any(need)) {
+          const float alpha = need ? ((m == kNegInf) ? 0.f : fast_exp2(m - mxs)) : 1.f;
+          m = need ? mxs : m;
+          l *= alpha;
+#pragma unroll
+          for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+        }
+        const float nm = (m == kNegInf) ? 0.f : -m;
+        // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
+        uint32_t pk[16];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s0[r], scale_log2, nm));
+          const float p1 = fast_exp2(__builtin_fmaf(s0[r + 1], scale_log2, nm));
+          const float p2 = fast_exp2(__builtin_fmaf(s1[r], scale_log2, nm));
+          const float p3 = fast_exp2(__builtin_fmaf(s1[r + 1], scale_log2, nm));
+          l += (p0 + p1) + (p2 + p3);
+          pk[r >> 1] = TT::pack2(p0, p1);
+          pk[8 + (r >> 1)] = TT::pack2(p2, p3);
+        }
+        // ---- O^T += V^T P^T, four 16-key steps
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          const u32x4_t bop = {pk[4 * t4 + 0], pk[4 * t4 + 1], pk[4 * t4 + 2], pk[4 * t4 + 3]};
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] = TT::mfma32(vop[t4][db], bop, oacc[db]);
+        }
+      }
+      const bool q_next = last && has_next;
+      if (q_next) load_q(cn);  // this item's Q is no longer read
+      // stream tile g+1 must have landed before the barrier; the loads issued
+      // after it (tile g+2's, the next item's Q) may stay in flight
+      if (issued) {
+        if (q_next)
+          __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * BPW + KS));
+        else
+          __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * BPW));
+      } else {
+        if (q_next)
+          __builtin_amdgcn_s_waitcnt(0x0F70 | KS);
+        else
+          vmem_wait_all();
+      }
+      lds_barrier();
+      stage = (stage == kRingStages - 1) ? 0 : stage + 1;
+    }
+
+    // ---- epilogue: combine half-wave denominators, normalise, store (rows past N_q dropped)
+    const auto rO = buffer_rsrc(O + ((int64_t)c.b * H_q + c.h) * (int64_t)N_q * D, head_q_bytes);
+    const float lt = half_sum(l);
+    const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = db * 32 + 8 * rg + 4 * lh;
+        const u32x2_t w = {TT::pack2(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv),
+                           TT::pack2(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv)};
+        buffer_store8(rO, (uint32_t)(c.qrow * D + d) * 2, w);
+      }
+    }
+    if (LSE != nullptr && lh == 0 && c.qrow < N_q) {
+      LSE[((int64_t)c.b * H_q + c.h) * N_q + c.qrow] = (lt > 0.f) ? (m + log2f(lt)) * kLn2 : kNegInf;
+    }
+    if (!has_next) break;
+    if (ntiles == 0) load_q(cn);  // (no tile step loaded it)
+    ++c_round;
+    cur = nwi;
+    c = ctx_of(cur);
+  }
+}
+
 // ---------------------------------------------------------------- fp32 inputs
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void prefill32_kernel(
@@ -1649,13 +1995,26 @@ inline int xcd_grid(int64_t items) { return (int)(((items + 7) / 8) * 8); }
 // With fewer than four items per slot the static zig-zag cannot balance
 // causal items of very different lengths, and the hardware's dynamic dispatch
 // of one item per workgroup does better; the persistent grid is used above that.
-template <class TT, int D, int NW, bool CAUSAL>
+// Which form of the default kernel runs: the ring form for d = 64, the
+// register-staged form for d = 128 (measured on the two shapes' workloads; at
+// d = 128 the two are within noise of each other).
+template <int D> constexpr bool kRingDefault = (D == 64);
+
+template <class TT, int D, bool CAUSAL, int NW, bool PERSIST, bool RING>
+constexpr auto prefill16_form() {
+  if constexpr (RING)
+    return prefill16_ring_kernel<TT, D, CAUSAL, NW, PERSIST>;
+  else
+    return prefill16_kernel<TT, D, CAUSAL, 1, NW, PERSIST>;
+}
+
+template <class TT, int D, int NW, bool CAUSAL, bool RING>
 hipError_t launch16pers_t(const PrefillArgs& a, hipStream_t st, int nqb, const int* kv_lens = nullptr,
                           int row_period = 0) {
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill16_kernel<TT, D, CAUSAL, 1, NW, true>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill16_form<TT, D, CAUSAL, NW, true, RING>(),
                                                      64 * NW, 0) != hipSuccess || n < 1)
       n = 1;
     per_cu = n;
@@ -1668,12 +2027,12 @@ hipError_t launch16pers_t(const PrefillArgs& a, hipStream_t st, int nqb, const i
   if (forced > 0) slots = forced < slots ? forced : slots;
   const float sl2 = a.scale * kLog2e;
   if (forced <= 0 && items < 4 * slots) {
-    hipLaunchKernelGGL((prefill16_kernel<TT, D, CAUSAL, 1, NW, false>), dim3(xcd_grid(items)),
+    hipLaunchKernelGGL((prefill16_form<TT, D, CAUSAL, NW, false, RING>()), dim3(xcd_grid(items)),
                        dim3(64 * NW), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2,
                        nqb, a.B, kv_lens, row_period);
   } else {
-    hipLaunchKernelGGL((prefill16_kernel<TT, D, CAUSAL, 1, NW, true>), dim3(xcd_grid(slots)),
+    hipLaunchKernelGGL((prefill16_form<TT, D, CAUSAL, NW, true, RING>()), dim3(xcd_grid(slots)),
                        dim3(64 * NW), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2,
                        nqb, a.B, kv_lens, row_period);
@@ -1681,12 +2040,12 @@ hipError_t launch16pers_t(const PrefillArgs& a, hipStream_t st, int nqb, const i
   return hipGetLastError();
 }
 
-template <class TT, int D, int NW>
+template <class TT, int D, int NW, bool RING = false>
 hipError_t launch16pers(const PrefillArgs& a, hipStream_t st, const int* kv_lens = nullptr,
                         int row_period = 0) {
   const int nqb = (a.N_q + NW * 32 - 1) / (NW * 32);
-  return a.causal ? launch16pers_t<TT, D, NW, true>(a, st, nqb, kv_lens, row_period)
-                  : launch16pers_t<TT, D, NW, false>(a, st, nqb, kv_lens, row_period);
+  return a.causal ? launch16pers_t<TT, D, NW, true, RING>(a, st, nqb, kv_lens, row_period)
+                  : launch16pers_t<TT, D, NW, false, RING>(a, st, nqb, kv_lens, row_period);
 }
 
 template <class TT, int D, int QB, int NW = 4>
@@ -1788,7 +2147,8 @@ hipError_t launch16w2(const PrefillArgs& a, hipStream_t st) {
 // scores, 4 = two ping-ponging wavefront groups, 5 = direct-load 3-stage ring,
 // 6 = two query blocks with a direct-load ring, 7 = 8 wavefronts, 8 = the
 // default kernel with one work item per workgroup instead of a persistent grid,
-// 9 = two wavefront groups skewed by half a tile.
+// 9 = two wavefront groups skewed by half a tile, 10 = the default kernel's ring
+// form (direct loads), 11 = its register-staged form.
 template <class TT, int D>
 hipError_t launch16skew(const PrefillArgs& a, hipStream_t st) {
   const int nqb = (a.N_q + 255) / 256;
@@ -1820,7 +2180,9 @@ hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
   if (variant == 7) return launch16q<TT, D, 1, 8>(a, st);
   if (variant == 8) return launch16q<TT, D, 1, (D == 128 ? 8 : 4)>(a, st);
   if (variant == 9) return launch16skew<TT, D>(a, st);
-  return launch16pers<TT, D, (D == 128 ? 8 : 4)>(a, st);
+  if (variant == 10) return launch16pers<TT, D, (D == 128 ? 8 : 4), true>(a, st);
+  if (variant == 11) return launch16pers<TT, D, (D == 128 ? 8 : 4), false>(a, st);
+  return launch16pers<TT, D, (D == 128 ? 8 : 4), kRingDefault<D>>(a, st);
 }
 
 template <int D>
@@ -1847,11 +2209,25 @@ hipError_t launch32(const PrefillArgs& a, hipStream_t st) {
 // lengths; see prefill16_kernel).
 hipError_t launch_prefill_rows(const PrefillArgs& a, const int* kv_lens, int row_period,
                                hipStream_t st) {
+  const char* env = getenv("ATTN_PREFILL_VARIANT");
+  const int variant = env ? atoi(env) : 0;
+  if (variant == 10 || variant == 11) {  // tuning and testing: force the ring or the staged form
+    const bool ring = variant == 10;
+    if (a.dtype == kDtypeBF16)
+      return a.d == 64 ? (ring ? launch16pers<BF16, 64, 4, true>(a, st, kv_lens, row_period)
+                               : launch16pers<BF16, 64, 4, false>(a, st, kv_lens, row_period))
+                       : (ring ? launch16pers<BF16, 128, 8, true>(a, st, kv_lens, row_period)
+                               : launch16pers<BF16, 128, 8, false>(a, st, kv_lens, row_period));
+    return a.d == 64 ? (ring ? launch16pers<F16, 64, 4, true>(a, st, kv_lens, row_period)
+                             : launch16pers<F16, 64, 4, false>(a, st, kv_lens, row_period))
+                     : (ring ? launch16pers<F16, 128, 8, true>(a, st, kv_lens, row_period)
+                             : launch16pers<F16, 128, 8, false>(a, st, kv_lens, row_period));
+  }
   if (a.dtype == kDtypeBF16)
-    return a.d == 64 ? launch16pers<BF16, 64, 4>(a, st, kv_lens, row_period)
-                     : launch16pers<BF16, 128, 8>(a, st, kv_lens, row_period);
-  return a.d == 64 ? launch16pers<F16, 64, 4>(a, st, kv_lens, row_period)
-                   : launch16pers<F16, 128, 8>(a, st, kv_lens, row_period);
+    return a.d == 64 ? launch16pers<BF16, 64, 4, kRingDefault<64>>(a, st, kv_lens, row_period)
+                     : launch16pers<BF16, 128, 8, kRingDefault<128>>(a, st, kv_lens, row_period);
+  return a.d == 64 ? launch16pers<F16, 64, 4, kRingDefault<64>>(a, st, kv_lens, row_period)
+                   : launch16pers<F16, 128, 8, kRingDefault<128>>(a, st, kv_lens, row_period);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {

@@ -189,3 +189,15 @@ def test_decode_rows_mode_chosen_for_tall_batches():
     """64 requests x 4 KV heads x (8 heads x 16 tokens) rows: rows mode by default."""
     lens = np.random.default_rng(3).integers(1, 2001, size=64).astype(np.int32)
     _decode_case(64, 32, 4, 2000, 128, "bf16", lens, seed=95, Nq=16, causal=True)
+
+
+@pytest.mark.parametrize("form", ["10", "11"], ids=["ring", "staged"])
+@pytest.mark.parametrize("case", [MULTI[2], MULTI[4], MULTI[7]], ids=lambda c: "x".join(map(str, c[:6])))
+def test_decode_rows_mode_both_kernel_forms(case, form, monkeypatch):
+    """Rows mode through either form of the prefill kernel (K/V tiles streamed
+    by direct loads, or staged through registers)."""
+    monkeypatch.setenv("ATTN_DECODE_ROWS_MODE", "1")
+    monkeypatch.setenv("ATTN_PREFILL_VARIANT", form)
+    B, Hq, Hkv, Nkv, d, Nq, lens = case
+    _decode_case(B, Hq, Hkv, Nkv, d, "bf16", lens,
+                 seed=zlib.crc32(repr((case, form)).encode()) % 10000, Nq=Nq, causal=True)

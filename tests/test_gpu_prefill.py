@@ -162,18 +162,22 @@ def test_prefill_full_size_sampled(cid):
 MANY_ITEMS = [(2, 64, 64, 700, 700, 128), (4, 64, 16, 500, 500, 64), (1, 48, 8, 1100, 2000, 128)]
 
 
+@pytest.mark.parametrize("form", [None, "10", "11"], ids=["default", "ring", "staged"])
 @pytest.mark.parametrize("slots", [None, "16", "8"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", MANY_ITEMS, ids=lambda s: "x".join(map(str, s)))
-def test_prefill_persistent_grid_many_items(shape, causal, slots, monkeypatch):
+def test_prefill_persistent_grid_many_items(shape, causal, slots, form, monkeypatch):
     """Several items per workgroup: a persistent grid of 8 or 16 workgroups (or
-    the automatic choice) walks every query block exactly once."""
+    the automatic choice) walks every query block exactly once, with the K/V
+    tiles staged through registers or streamed by direct loads across items."""
     if slots is not None:
         monkeypatch.setenv("ATTN_PREFILL_SLOTS", slots)
+    if form is not None:
+        monkeypatch.setenv("ATTN_PREFILL_VARIANT", form)
     _run_small(*shape, "bf16", causal, seed=zlib.crc32(repr((shape, causal)).encode()) % 10000)
 
 
-@pytest.mark.parametrize("variant", ["1", "2", "3", "4", "5", "6", "7", "8", "9"])
+@pytest.mark.parametrize("variant", ["1", "2", "3", "4", "5", "6", "7", "8", "9", "10", "11"])
 def test_prefill_variants_match_oracle(variant, monkeypatch):
     """Every alternative kernel behind ATTN_PREFILL_VARIANT (tuning only) meets
     the same bar as the default."""
