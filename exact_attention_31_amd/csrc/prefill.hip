@@ -38,9 +38,9 @@ namespace attn {
 
 namespace {
 
-constexpr int kBM = 128;  // query rows per workgroup (4 wavefronts x 32)
-constexpr int kBN = 64;   // keys per tile
-constexpr int kThreads = 256;
+constexpr int kBN = 64;        // keys per tile
+constexpr int kBM = 128;       // fp32 kernel: query rows per workgroup (4 wavefronts x 32)
+constexpr int kThreads = 256;  // fp32 kernel: threads per workgroup
 
 // Row stride (elements) of the K and V tiles in LDS (64 banks of 4 bytes).
 // K: rows 68 dwords apart, so the 16-byte reads of 16 consecutive rows cover
@@ -58,9 +58,10 @@ template <int D> struct Lds16 {
 // common reference point, so u / l is unchanged.
 constexpr float kLazyRescale = 8.f;
 
-// QB query blocks of 32 rows per wavefront (QB = 1: 128 rows per workgroup,
-// QB = 2: 256). Each K or V operand read from LDS feeds QB MFMAs, so QB = 2
-// halves the LDS bytes per FLOP at the price of twice the registers.
+// QB query blocks of 32 rows per wavefront (NW * 32 * QB rows per
+// workgroup). Each K or V operand read from LDS feeds QB MFMAs, so QB = 2
+// halves the LDS bytes per FLOP at the price of twice the registers (a tuning
+// alternative only: at d = 128 it spills).
 // Workgroup -> (batch, head, query block). Workgroups are handed to the 8
 // XCDs (each with its own L2) round-robin by linear id, so XCD x runs ids
 // x, x+8, x+16, ... Work items (head-major, longest query block first within a
@@ -423,1114 +424,25 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
   }
 }
 
-// Phase-skewed form: 8 wavefronts, two per SIMD (wavefronts w and w + 4 share
-// a SIMD). Group A (wavefronts 0-3) works tile t as S(t) -> softmax(t) ->
-// PV(t); group B (4-7) runs half a tile behind: softmax(t-1) -> PV(t-1) ->
-// S(t), carrying its scores across the barrier. So while one wavefront of a
-// SIMD turns scores into probabilities on the vector ALUs, the other keeps the
-// matrix cores busy, instead of both doing the same phase at once. V tiles are
-// read one iteration longer (by group B), so V has three LDS buffers and K two;
-// one extra iteration at the end lets group B finish the last tile.
-template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void prefill16_skew_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
-    float scale_log2, int nqb, int nbatch) {
-  constexpr int KST = Lds16<D>::kK;
-  constexpr int VST = Lds16<D>::kV;
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int NT = 512;
-  constexpr int LPT = kBN * CPR / NT;
-  constexpr int BM = 256;
-  static_assert(LPT >= 1 && LPT * NT == kBN * CPR, "tile load must split evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[3][kBN * VST];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool grpB = wave >= 4;
-  const int lr = lane & 31;
-  const int lh = lane >> 5;
-  const WorkItem wi = map_work(nqb, H_q, nbatch, CAUSAL);
-  if (!wi.valid) return;
-  const int qblk = wi.qblk, h = wi.h, b = wi.b;
-  const int hk = h / (H_q / H_kv);
-  const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
-  const uint32_t head_kv_bytes = (uint32_t)N_kv * D * 2;
-  const auto rQ = buffer_rsrc(Q + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
-  const auto rK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-  const auto rV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-  const int q0 = qblk * BM + wave * 32;
-  const int off = N_kv - N_q;
-  const int qrow = q0 + lr;
-  const int lim = CAUSAL ? min(N_kv, max(qrow + off + 1, 0)) : N_kv;
-
-  u32x4_t qreg[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st) qreg[st] = buffer_load16(rQ, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
-
-  int kv_end = N_kv;
-  if (CAUSAL) {
-    const int qlast = min(qblk * BM + BM - 1, N_q - 1);
-    kv_end = min(N_kv, qlast + off + 1);
-  }
-  const int ntiles = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
-
-  uint32_t ld_off[LPT];
-  int st_k[LPT], st_v[LPT];
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int c = tid + NT * i;
-    const int r = c / CPR, cc = c % CPR;
-    ld_off[i] = (uint32_t)(r * D + cc * 8) * 2;
-    st_k[i] = r * KST + cc * 8;
-    st_v[i] = r * VST + cc * 8;
-  }
-  const int k_lane = lr * KST + 8 * lh;
-  const int v_lane = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * VST + 16 * ((lane >> 4) & 1) +
-                     4 * (lane & 3);
-  u32x4_t kbuf[LPT], vbuf[LPT];
-  auto load_tile = [&](int t) {
-    const uint32_t base = (uint32_t)(t * kBN) * D * 2;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      kbuf[i] = buffer_load16(rK, base + ld_off[i]);
-      vbuf[i] = buffer_load16(rV, base + ld_off[i]);
-    }
-  };
-  auto store_tile = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      *(u32x4_t*)(&sK[t & 1][st_k[i]]) = kbuf[i];
-      *(u32x4_t*)(&sV[t % 3][st_v[i]]) = vbuf[i];
-    }
-  };
-
-  f32x16_t oacc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16_t{0};
-  float m = kNegInf, l = 0.f;
-
-  // does tile t hold any key visible to this wavefront?
-  auto live = [&](int t) { return !CAUSAL || t * kBN <= q0 + 31 + off; };
-  auto scores = [&](int t, f32x16_t& s0, f32x16_t& s1) {
-    const uint16_t* tK = &sK[t & 1][0] + k_lane;
-    s0 = f32x16_t{0};
-    s1 = f32x16_t{0};
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      const u32x4_t a0 = *(const u32x4_t*)(tK + 16 * st);
-      const u32x4_t a1 = *(const u32x4_t*)(tK + 32 * KST + 16 * st);
-      s0 = TT::mfma32(a0, qreg[st], s0);
-      s1 = TT::mfma32(a1, qreg[st], s1);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int st = 0; st < KS - 2; ++st) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  };
-  // softmax of the scores in s0/s1 (tile t) and O^T += V(t)^T P^T
-  auto softmax_pv = [&](int t, f32x16_t& s0, f32x16_t& s1) {
-    const uint16_t* tV = &sV[t % 3][0] + v_lane;
-    const int kv0 = t * kBN;
-    const bool need_mask = (kv0 + kBN > N_kv) || (CAUSAL && kv0 + kBN - 1 > q0 + off);
-    if (need_mask) {
-      const int rel = lim - (kv0 + 4 * lh);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int e = 8 * (r >> 2) + (r & 3);
-        s0[r] = (e < rel) ? s0[r] : kNegInf;
-        s1[r] = (e + 32 < rel) ? s1[r] : kNegInf;
-      }
-    }
-    float mx = max3(s0[0], s0[1], s1[0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = max3(mx, s0[r], s1[r]);
-    mx = fmaxf(mx, s1[0]);
-    const float mxs = half_max(mx) * scale_log2;
-    const bool need = mxs > m + kLazyRescale;
-    if (wave_any(need)) {
-      const float alpha = need ? ((m == kNegInf) ? 0.f : fast_exp2(m - mxs)) : 1.f;
-      m = need ? mxs : m;
-      l *= alpha;
-#pragma unroll
-      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-    }
-    const float nm = (m == kNegInf) ? 0.f : -m;
-    uint32_t pk[16];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = fast_exp2(__builtin_fmaf(s0[r], scale_log2, nm));
-      const float p1 = fast_exp2(__builtin_fmaf(s0[r + 1], scale_log2, nm));
-      const float p2 = fast_exp2(__builtin_fmaf(s1[r], scale_log2, nm));
-      const float p3 = fast_exp2(__builtin_fmaf(s1[r + 1], scale_log2, nm));
-      l += (p0 + p1) + (p2 + p3);
-      pk[r >> 1] = TT::pack2(p0, p1);
-      pk[8 + (r >> 1)] = TT::pack2(p2, p3);
-    }
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const u32x4_t bop = {pk[4 * t4 + 0], pk[4 * t4 + 1], pk[4 * t4 + 2], pk[4 * t4 + 3]};
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x2_t lo = lds_read_tr16(tV + 16 * t4 * VST + db * 32);
-        const u32x2_t hi = lds_read_tr16(tV + (16 * t4 + 8) * VST + db * 32);
-        oacc[db] = TT::mfma32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, bop, oacc[db]);
-      }
-    }
-    // V operand reads two MFMAs ahead of their use
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * DB - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-  };
-
-  load_tile(0);
-  store_tile(0);
-  vmem_wait_all();
-  __syncthreads();
-
-  // The two groups run separate loops (so that group B's carried scores do not
-  // occupy registers in group A's code); both pass the same barriers.
-  const int niter = ntiles > 0 ? ntiles + 1 : 0;
-  if (grpB) {
-    f32x16_t c0 = f32x16_t{0}, c1 = f32x16_t{0};  // scores carried to the next iteration
-    for (int t = 0; t < niter; ++t) {
-      if (t + 1 < ntiles) load_tile(t + 1);
-      if (t >= 1 && live(t - 1)) softmax_pv(t - 1, c0, c1);
-      if (t < ntiles && live(t)) scores(t, c0, c1);
-      if (t + 1 < ntiles) store_tile(t + 1);
-      __syncthreads();
-    }
-  } else {
-    for (int t = 0; t < niter; ++t) {
-      if (t + 1 < ntiles) load_tile(t + 1);
-      if (t < ntiles && live(t)) {
-        f32x16_t a0, a1;
-        scores(t, a0, a1);
-        softmax_pv(t, a0, a1);
-      }
-      if (t + 1 < ntiles) store_tile(t + 1);
-      __syncthreads();
-    }
-  }
-
-  const auto rO = buffer_rsrc(O + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
-  const float lt = half_sum(l);
-  const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d = db * 32 + 8 * rg + 4 * lh;
-      const u32x2_t w = {TT::pack2(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv),
-                         TT::pack2(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv)};
-      buffer_store8(rO, (uint32_t)(qrow * D + d) * 2, w);
-    }
-  }
-  if (LSE != nullptr && lh == 0 && qrow < N_q) {
-    LSE[((int64_t)b * H_q + h) * N_q + qrow] = (lt > 0.f) ? (m + log2f(lt)) * kLn2 : kNegInf;
-  }
-}
-
-// Software-pipelined form (32 rows per wavefront). While the matrix cores
-// compute the scores of key tile t+1, the vector ALUs turn the scores of tile t
-// into probabilities; the products with V follow. K is staged in LDS one tile
-// ahead of V, so the same two buffers per tensor suffice:
-//   iteration t reads K(t+1) from K buffer (t+1)%2 and V(t) from V buffer t%2,
-//   and at its end stores K(t+2) into K buffer t%2 and V(t+1) into V buffer
-//   (t+1)%2, both loaded from HBM while the tile's math runs.
-template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void prefill16_pipe_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
-    float scale_log2, int nqb, int nbatch) {
-  constexpr int KST = Lds16<D>::kK;
-  constexpr int VST = Lds16<D>::kV;
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int LPT = kBN * CPR / kThreads;
-  static_assert(LPT * kThreads == kBN * CPR, "tile load must split evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBN * VST];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 31;
-  const int lh = lane >> 5;
-  const WorkItem wi = map_work(nqb, H_q, nbatch, CAUSAL);
-  if (!wi.valid) return;
-  const int qblk = wi.qblk, h = wi.h, b = wi.b;
-  const int hk = h / (H_q / H_kv);
-
-  const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
-  const uint32_t head_kv_bytes = (uint32_t)N_kv * D * 2;
-  const auto rQ = buffer_rsrc(Q + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
-  const auto rK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-  const auto rV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-
-  const int q0 = qblk * kBM + wave * 32;
-  const int qrow = q0 + lr;
-  const int off = N_kv - N_q;
-  const int lim = CAUSAL ? min(N_kv, max(qrow + off + 1, 0)) : N_kv;
-
-  u32x4_t qreg[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st) qreg[st] = buffer_load16(rQ, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
-
-  int kv_end = N_kv;
-  if (CAUSAL) kv_end = min(N_kv, min(qblk * kBM + kBM - 1, N_q - 1) + off + 1);
-  const int ntiles = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
-  // tiles holding a key visible to some row of this wavefront (a prefix of the tiles)
-  int wtiles = ntiles;
-  if (CAUSAL) wtiles = min(ntiles, max(0, (q0 + 31 + off + kBN) / kBN));
-
-  uint32_t ld_off[LPT];
-  int st_k[LPT], st_v[LPT];
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int c = tid + kThreads * i;
-    const int r = c / CPR, cc = c % CPR;
-    ld_off[i] = (uint32_t)(r * D + cc * 8) * 2;
-    st_k[i] = r * KST + cc * 8;
-    st_v[i] = r * VST + cc * 8;
-  }
-  const int k_lane = lr * KST + 8 * lh;
-  const int v_lane = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * VST + 16 * ((lane >> 4) & 1) +
-                     4 * (lane & 3);
-  u32x4_t kbuf[LPT], vbuf[LPT];
-  auto load_k = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) kbuf[i] = buffer_load16(rK, (uint32_t)(t * kBN) * D * 2 + ld_off[i]);
-  };
-  auto load_v = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) vbuf[i] = buffer_load16(rV, (uint32_t)(t * kBN) * D * 2 + ld_off[i]);
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) *(u32x4_t*)(&sK[buf][st_k[i]]) = kbuf[i];
-  };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) *(u32x4_t*)(&sV[buf][st_v[i]]) = vbuf[i];
-  };
-  auto gemm_s = [&](int buf, f32x16_t& s0, f32x16_t& s1) {
-    const uint16_t* tK = &sK[0][0] + buf * (kBN * KST) + k_lane;
-    s0 = f32x16_t{0};
-    s1 = f32x16_t{0};
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      const u32x4_t a0 = *(const u32x4_t*)(tK + 16 * st);
-      const u32x4_t a1 = *(const u32x4_t*)(tK + 32 * KST + 16 * st);
-      s0 = TT::mfma32(a0, qreg[st], s0);
-      s1 = TT::mfma32(a1, qreg[st], s1);
-    }
-  };
-
-  // prologue: K(0), V(0) into buffers 0 and K(1) into K buffer 1 (past-the-end
-  // loads read zeros, so this needs no branch)
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
-  load_k(1);
-  store_k(1);
-  vmem_wait_all();
-  __syncthreads();
-
-  f32x16_t oacc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16_t{0};
-  float m = kNegInf, l = 0.f;
-  f32x16_t sa0, sa1, sb0, sb1;
-  gemm_s(0, sa0, sa1);
-
-  auto step = [&](int t, f32x16_t& c0, f32x16_t& c1, f32x16_t& n0, f32x16_t& n1) {
-    const bool pre_k = t + 2 < ntiles;
-    const bool pre_v = t + 1 < ntiles;
-    if (pre_k) load_k(t + 2);
-    if (pre_v) load_v(t + 1);
-    if (t < wtiles) {
-      const int kv0 = t * kBN;
-      // ---- mask, row max and rescale decision for S(t)
-      const bool need_mask = (kv0 + kBN > N_kv) || (CAUSAL && kv0 + kBN - 1 > q0 + off);
-      if (need_mask) {
-        const int kvb = kv0 + 4 * lh;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kv = kvb + 8 * (r >> 2) + (r & 3);
-          c0[r] = (kv < lim) ? c0[r] : kNegInf;
-          c1[r] = (kv + 32 < lim) ? c1[r] : kNegInf;
-        }
-      }
-      float mx = max3(c0[0], c0[1], c1[0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = max3(mx, c0[r], c1[r]);
-      const float mxs = half_max(mx) * scale_log2;
-      const bool need = mxs > m + kLazyRescale;
-      if (wave_any(need)) {
-        const float alpha = need ? ((m == kNegInf) ? 0.f : fast_exp2(m - mxs)) : 1.f;
-        m = need ? mxs : m;
-        l *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-      }
-      const float nm = (m == kNegInf) ? 0.f : -m;
-      // ---- S(t+1) on the matrix cores while S(t) becomes P(t)
-      gemm_s((t + 1) & 1, n0, n1);
-      uint32_t pk[16];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(c0[r], scale_log2, nm));
-        const float p1 = fast_exp2(__builtin_fmaf(c0[r + 1], scale_log2, nm));
-        const float p2 = fast_exp2(__builtin_fmaf(c1[r], scale_log2, nm));
-        const float p3 = fast_exp2(__builtin_fmaf(c1[r + 1], scale_log2, nm));
-        l += (p0 + p1) + (p2 + p3);
-        pk[r >> 1] = TT::pack2(p0, p1);
-        pk[8 + (r >> 1)] = TT::pack2(p2, p3);
-      }
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads of K
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two score MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x002, 56 / KS * 2, 0);  // exp / convert / sum
-      }
-      // ---- O^T += V^T P^T
-      const uint16_t* tV = &sV[0][0] + (t & 1) * (kBN * VST) + v_lane;
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const u32x4_t bop = {pk[4 * t4 + 0], pk[4 * t4 + 1], pk[4 * t4 + 2], pk[4 * t4 + 3]};
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2_t lo = lds_read_tr16(tV + 16 * t4 * VST + db * 32);
-          const u32x2_t hi = lds_read_tr16(tV + (16 * t4 + 8) * VST + db * 32);
-          const u32x4_t aop = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = TT::mfma32(aop, bop, oacc[db]);
-        }
-      }
-    }
-    if (pre_k) store_k(t & 1);
-    if (pre_v) store_v((t + 1) & 1);
-    __syncthreads();
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, sa0, sa1, sb0, sb1);
-    if (t + 1 < ntiles) step(t + 1, sb0, sb1, sa0, sa1);
-  }
-
-  l = half_sum(l);
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
-  const auto rO = buffer_rsrc(O + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d = db * 32 + 8 * rg + 4 * lh;
-      const u32x2_t w = {TT::pack2(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv),
-                         TT::pack2(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv)};
-      buffer_store8(rO, (uint32_t)(qrow * D + d) * 2, w);
-    }
-  }
-  if (LSE != nullptr && lh == 0 && qrow < N_q) {
-    LSE[((int64_t)b * H_q + h) * N_q + qrow] = (l > 0.f) ? (m + log2f(l)) * kLn2 : kNegInf;
-  }
-}
-
-// Two-group form: 8 wavefronts (two per SIMD) share each K/V tile; 256 query
-// rows per workgroup, 32 per wavefront. Every tile t is worked in two phases:
-//   X(t): scores of tile t+1 on the matrix cores, interleaved with the
-//         softmax of tile t on the vector ALUs;
-//   Y(t): O += V(t) P(t) on the matrix cores.
-// Group 0 (wavefronts 0-3) runs X(t) while group 1 (wavefronts 4-7) runs
-// Y(t-1), and then Y(t) while group 1 runs X(t), so on each SIMD one
-// wavefront's vector work overlaps the other's matrix work. Phases are
-// separated by workgroup barriers ("half-steps" h = 0 .. 2*ntiles).
-// LDS holds two K and two V tiles, rotated as described at the prologue.
-constexpr int kPPThreads = 512;
-constexpr int kPPBM = 256;
-
-template <class TT, int D, bool CAUSAL, bool PIPE>
-__global__ __launch_bounds__(kPPThreads, 1) void prefill16_pp_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
-    float scale_log2, int nqb, int nbatch) {
-  constexpr int KST = Lds16<D>::kK;
-  constexpr int VST = Lds16<D>::kV;
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int LPT = kBN * CPR / kPPThreads;
-  static_assert(LPT >= 1 && LPT * kPPThreads == kBN * CPR, "tile load must split evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBN * VST];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
-  const int lr = lane & 31;
-  const int lh = lane >> 5;
-  const WorkItem wi = map_work(nqb, H_q, nbatch, CAUSAL);
-  if (!wi.valid) return;
-  const int qblk = wi.qblk, h = wi.h, b = wi.b;
-  const int hk = h / (H_q / H_kv);
-
-  const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
-  const uint32_t head_kv_bytes = (uint32_t)N_kv * D * 2;
-  const auto rQ = buffer_rsrc(Q + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
-  const auto rK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-  const auto rV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-
-  const int q0 = qblk * kPPBM + wave * 32;
-  const int qrow = q0 + lr;
-  const int off = N_kv - N_q;
-  const int lim = CAUSAL ? min(N_kv, max(qrow + off + 1, 0)) : N_kv;
-
-  u32x4_t qreg[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st) qreg[st] = buffer_load16(rQ, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
-
-  int kv_end = N_kv;
-  if (CAUSAL) kv_end = min(N_kv, min(qblk * kPPBM + kPPBM - 1, N_q - 1) + off + 1);
-  const int ntiles = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
-  int wtiles = ntiles;  // tiles holding a key visible to some row of this wavefront
-  if (CAUSAL) wtiles = min(ntiles, max(0, (q0 + 31 + off + kBN) / kBN));
-
-  uint32_t ld_off[LPT];
-  int st_k[LPT], st_v[LPT];
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int c = tid + kPPThreads * i;
-    const int r = c / CPR, cc = c % CPR;
-    ld_off[i] = (uint32_t)(r * D + cc * 8) * 2;
-    st_k[i] = r * KST + cc * 8;
-    st_v[i] = r * VST + cc * 8;
-  }
-  const int k_lane = lr * KST + 8 * lh;
-  const int v_lane = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * VST + 16 * ((lane >> 4) & 1) +
-                     4 * (lane & 3);
-  u32x4_t kbuf[LPT], vbuf[LPT];
-  auto load_k = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) kbuf[i] = buffer_load16(rK, (uint32_t)(t * kBN) * D * 2 + ld_off[i]);
-  };
-  auto load_v = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) vbuf[i] = buffer_load16(rV, (uint32_t)(t * kBN) * D * 2 + ld_off[i]);
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) *(u32x4_t*)(&sK[buf][st_k[i]]) = kbuf[i];
-  };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) *(u32x4_t*)(&sV[buf][st_v[i]]) = vbuf[i];
-  };
-
-  // K look-ahead: with PIPE, X(t) reads K(t+1), else K(t). Buffer schedule:
-  //   end of even half-step 2t: store K(t+KA) into K buffer (t+KA)%2, whose
-  //     previous tile K(t+KA-2) was last read in half-step 2t-1;
-  //   end of odd half-step 2t+1: store V(t+1) into V buffer (t+1)%2, whose
-  //     previous tile V(t-1) was last read (group 1, Y(t-1)) in half-step 2t.
-  // K(t+KA+1) is loaded at the start of half-step 2t+1, V(t+1) at the start of 2t.
-  constexpr int KA = PIPE ? 2 : 1;
-  // prologue: K(0..KA-1), V(0) in LDS, K(KA) in flight
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
-  if constexpr (PIPE) {
-    load_k(1);
-    store_k(1);
-  }
-  load_k(KA);
-  vmem_wait_all();
-  __syncthreads();
-
-  f32x16_t oacc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16_t{0};
-  float m = kNegInf, l = 0.f;
-  f32x16_t sc0, sc1;  // scores of the tile being turned into probabilities
-  uint32_t pk[16];    // its probabilities, 16-bit pairs, B operand of P V
-  if constexpr (PIPE) {
-    const uint16_t* tK = &sK[0][0] + k_lane;
-    sc0 = f32x16_t{0};
-    sc1 = f32x16_t{0};
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      sc0 = TT::mfma32(*(const u32x4_t*)(tK + 16 * st), qreg[st], sc0);
-      sc1 = TT::mfma32(*(const u32x4_t*)(tK + 32 * KST + 16 * st), qreg[st], sc1);
-    }
-  }
-
-  // X(t): softmax of S(t) -> pk. With PIPE, S(t+1) = K(t+1) Q^T is computed on
-  // the matrix cores in the same phase (interleaved with the softmax); without
-  // it, S(t) is computed at the start of X(t).
-  auto phase_x = [&](int t) {
-    const int kv0 = t * kBN;
-    if constexpr (!PIPE) {
-      const uint16_t* tK = &sK[0][0] + (t & 1) * (kBN * KST) + k_lane;
-      sc0 = f32x16_t{0};
-      sc1 = f32x16_t{0};
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        sc0 = TT::mfma32(*(const u32x4_t*)(tK + 16 * st), qreg[st], sc0);
-        sc1 = TT::mfma32(*(const u32x4_t*)(tK + 32 * KST + 16 * st), qreg[st], sc1);
-      }
-    }
-    const bool need_mask = (kv0 + kBN > N_kv) || (CAUSAL && kv0 + kBN - 1 > q0 + off);
-    if (need_mask) {
-      const int kvb = kv0 + 4 * lh;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kv = kvb + 8 * (r >> 2) + (r & 3);
-        sc0[r] = (kv < lim) ? sc0[r] : kNegInf;
-        sc1[r] = (kv + 32 < lim) ? sc1[r] : kNegInf;
-      }
-    }
-    float mx = max3(sc0[0], sc0[1], sc1[0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = max3(mx, sc0[r], sc1[r]);
-    const float mxs = half_max(mx) * scale_log2;
-    const bool need = mxs > m + kLazyRescale;
-    if (wave_any(need)) {
-      const float alpha = need ? ((m == kNegInf) ? 0.f : fast_exp2(m - mxs)) : 1.f;
-      m = need ? mxs : m;
-      l *= alpha;
-#pragma unroll
-      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-    }
-    const float nm = (m == kNegInf) ? 0.f : -m;
-    f32x16_t n0 = f32x16_t{0}, n1 = f32x16_t{0};
-    if constexpr (PIPE) {
-      const uint16_t* tK = &sK[0][0] + ((t + 1) & 1) * (kBN * KST) + k_lane;
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        n0 = TT::mfma32(*(const u32x4_t*)(tK + 16 * st), qreg[st], n0);
-        n1 = TT::mfma32(*(const u32x4_t*)(tK + 32 * KST + 16 * st), qreg[st], n1);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = fast_exp2(__builtin_fmaf(sc0[r], scale_log2, nm));
-      const float p1 = fast_exp2(__builtin_fmaf(sc0[r + 1], scale_log2, nm));
-      const float p2 = fast_exp2(__builtin_fmaf(sc1[r], scale_log2, nm));
-      const float p3 = fast_exp2(__builtin_fmaf(sc1[r + 1], scale_log2, nm));
-      l += (p0 + p1) + (p2 + p3);
-      pk[r >> 1] = TT::pack2(p0, p1);
-      pk[8 + (r >> 1)] = TT::pack2(p2, p3);
-    }
-    if constexpr (PIPE) {
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads of K
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two score MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x002, 112 / KS, 0);  // softmax VALU
-      }
-      sc0 = n0;
-      sc1 = n1;
-    }
-  };
-  // Y(t): O^T += V(t)^T P(t)^T
-  auto phase_y = [&](int t) {
-    const uint16_t* tV = &sV[0][0] + (t & 1) * (kBN * VST) + v_lane;
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const u32x4_t bop = {pk[4 * t4 + 0], pk[4 * t4 + 1], pk[4 * t4 + 2], pk[4 * t4 + 3]};
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x2_t lo = lds_read_tr16(tV + 16 * t4 * VST + db * 32);
-        const u32x2_t hi = lds_read_tr16(tV + (16 * t4 + 8) * VST + db * 32);
-        const u32x4_t aop = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = TT::mfma32(aop, bop, oacc[db]);
-      }
-    }
-  };
-
-  const int nhalf = 2 * ntiles + 1;
-  for (int hs = 0; hs < nhalf; ++hs) {
-    const int t = hs >> 1;
-    const bool even = (hs & 1) == 0;
-    // HBM -> registers: V(t+1) at even half-steps, K(t+KA+1) at odd ones
-    if (even) {
-      if (t + 1 < ntiles) load_v(t + 1);
-    } else {
-      if (t + KA + 1 < ntiles) load_k(t + KA + 1);
-    }
-    // group 0: X(t) at even half-steps, Y(t) at odd; group 1: Y(t-1), then X(t)
-    const bool do_x = (grp == 0) == even;
-    const int tt = (grp == 1 && even) ? t - 1 : t;
-    if (tt >= 0 && tt < wtiles) {
-      if (do_x)
-        phase_x(tt);
-      else
-        phase_y(tt);
-    }
-    // registers -> LDS: K(t+KA) after even half-steps, V(t+1) after odd ones
-    if (even) {
-      if (t + KA < ntiles) store_k((t + KA) & 1);
-    } else {
-      if (t + 1 < ntiles) store_v((t + 1) & 1);
-    }
-    __syncthreads();
-  }
-
-  l = half_sum(l);
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
-  const auto rO = buffer_rsrc(O + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d = db * 32 + 8 * rg + 4 * lh;
-      const u32x2_t w = {TT::pack2(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv),
-                         TT::pack2(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv)};
-      buffer_store8(rO, (uint32_t)(qrow * D + d) * 2, w);
-    }
-  }
-  if (LSE != nullptr && lh == 0 && qrow < N_q) {
-    LSE[((int64_t)b * H_q + h) * N_q + qrow] = (l > 0.f) ? (m + log2f(l)) * kLn2 : kNegInf;
-  }
-}
-
-// Direct-load form: 32-key tiles streamed HBM -> LDS by buffer loads that
-// write LDS themselves (no staging registers), three tiles in a ring, so a tile
-// is requested two tiles before its use. LDS rows are unpadded and their
-// 16-byte chunks XOR-swizzled:
+// LDS layout of the ring form: K and V tiles of 64 keys, rows unpadded, their
+// 16-byte chunks XOR-swizzled so that both operand reads are conflict-free:
 //   K: chunk c of row r sits at c ^ ((r / RPB) % CPR): the 16 rows read by one
 //      16-lane slice of a score-MFMA operand fetch land on 16 distinct banks;
 //   V: chunk c of row r sits at c ^ 4*((r / RPB) % (4 / RPB)): the 4 rows of a
 //      transposing read land on distinct banks;
-// (RPB rows per 256-byte bank sweep, CPR chunks per row). One load instruction
-// fills 1 KB of LDS, lane j writing chunk j, so each lane fetches the logical
-// chunk that its physical slot holds.
-constexpr int kDLBN = 32;
-constexpr int kDLStages = 3;
-
-template <int D, int BN = kDLBN> struct DL {
-  static constexpr int RB = D * 2;
-  static constexpr int CPR = D / 8;
-  static constexpr int RPB = 256 / RB;
-  static constexpr int TILE = BN * RB;          // bytes per tensor tile
+// (RPB rows per 256-byte bank sweep, CPR chunks per row). One direct load
+// instruction fills 1 KB of LDS, lane j writing chunk j, so each lane fetches
+// the logical chunk that its physical slot holds.
+template <int D> struct RingLds {
+  static constexpr int RB = D * 2;              // bytes per row
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int RPB = 256 / RB;          // rows per 256-byte bank sweep
+  static constexpr int TILE = kBN * RB;         // bytes per tensor tile
   static constexpr int STAGE = 2 * TILE;        // K then V
   static constexpr int BLK = TILE / 1024;       // 1 KB load blocks per tensor tile
-  static constexpr int BPW = BLK / 4;           // per wavefront
   static __device__ __forceinline__ int kswz(int r) { return (r / RPB) & (CPR - 1); }
   static __device__ __forceinline__ int vswz(int r) { return 4 * ((r / RPB) & (RPB == 1 ? 3 : 1)); }
 };
-
-template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, (D == 128 ? 2 : 4)) void prefill16_dl_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
-    float scale_log2, int nqb, int nbatch) {
-  using L = DL<D>;
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  static_assert(L::BPW >= 1 && L::BPW * 4 == L::BLK, "tile must split over 4 wavefronts");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kDLStages * L::STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 31;
-  const int lh = lane >> 5;
-  const WorkItem wi = map_work(nqb, H_q, nbatch, CAUSAL);
-  if (!wi.valid) return;
-  const int qblk = wi.qblk, h = wi.h, b = wi.b;
-  const int hk = h / (H_q / H_kv);
-
-  const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
-  const uint32_t head_kv_bytes = (uint32_t)N_kv * D * 2;
-  const auto rQ = buffer_rsrc(Q + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
-  const auto rK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-  const auto rV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-
-  const int q0 = qblk * kBM + wave * 32;
-  const int qrow = q0 + lr;
-  const int off = N_kv - N_q;
-  const int lim = CAUSAL ? min(N_kv, max(qrow + off + 1, 0)) : N_kv;
-
-  u32x4_t qreg[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st) qreg[st] = buffer_load16(rQ, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
-
-  int kv_end = N_kv;
-  if (CAUSAL) kv_end = min(N_kv, min(qblk * kBM + kBM - 1, N_q - 1) + off + 1);
-  const int ntiles = kv_end > 0 ? (kv_end + kDLBN - 1) / kDLBN : 0;
-  int wtiles = ntiles;
-  if (CAUSAL) wtiles = min(ntiles, max(0, (q0 + 31 + off + kDLBN) / kDLBN));
-
-  // direct loads: block i of this wavefront -> LDS bytes [blk*1024, +1024) of the
-  // tile; lane j writes physical chunk p = blk*64 + j = (row p / CPR, slot p % CPR)
-  uint32_t kg_off[L::BPW], vg_off[L::BPW];
-#pragma unroll
-  for (int i = 0; i < L::BPW; ++i) {
-    const int p = (wave * L::BPW + i) * 64 + lane;
-    const int r = p / L::CPR, slot = p % L::CPR;
-    kg_off[i] = (uint32_t)(r * L::RB + ((slot ^ L::kswz(r)) * 16));
-    vg_off[i] = (uint32_t)(r * L::RB + ((slot ^ L::vswz(r)) * 16));
-  }
-  const auto dK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-  const auto dV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  auto issue_tile = [&](int t) {
-    const int stage = t % kDLStages;
-    const uint32_t g0 = (uint32_t)(t * kDLBN) * L::RB;
-#pragma unroll
-    for (int i = 0; i < L::BPW; ++i) {
-      const uint32_t kd = lds0 + stage * L::STAGE + (wave * L::BPW + i) * 1024;
-      dma_load16(dK, g0 + kg_off[i], kd);
-      dma_load16(dV, g0 + vg_off[i], kd + L::TILE);
-    }
-  };
-  // operand addresses within a stage (bytes)
-  //   K (score A operand): row lr, logical chunk 2*st + lh
-  //   V (transposing read): row 16*t4 + 4*lh + gi/4 (+8), logical chunk
-  //     4*db + 2*(g&1) + (gi&3)/2, 8-byte half gi&1
-  int ka[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st) ka[st] = lr * L::RB + (((2 * st + lh) ^ L::kswz(lr)) * 16);
-  const int g = lane >> 4, gi = lane & 15;
-  const int vrow = 4 * (g >> 1) + (gi >> 2);  // plus 16*t4 (+8); the swizzle only sees vrow % 4 (or % 8)
-  int va[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-    va[db] = L::TILE + vrow * L::RB + (((4 * db + 2 * (g & 1) + ((gi & 3) >> 1)) ^ L::vswz(vrow)) * 16) +
-             8 * (gi & 1);
-
-  issue_tile(0);
-  if (ntiles > 1) issue_tile(1);
-  vmem_wait_all();
-  __syncthreads();
-
-  f32x16_t oacc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16_t{0};
-  float m = kNegInf, l = 0.f;
-
-  for (int t = 0; t < ntiles; ++t) {
-    const bool ahead = t + 2 < ntiles;
-    if (ahead) issue_tile(t + 2);
-    if (t < wtiles) {
-      const uint8_t* st_base = smem + (t % kDLStages) * L::STAGE;
-      const int kv0 = t * kDLBN;
-      f32x16_t s0 = f32x16_t{0};
-#pragma unroll
-      for (int st = 0; st < KS; ++st) s0 = TT::mfma32(*(const u32x4_t*)(st_base + ka[st]), qreg[st], s0);
-      const bool need_mask = (kv0 + kDLBN > N_kv) || (CAUSAL && kv0 + kDLBN - 1 > q0 + off);
-      if (need_mask) {
-        const int kvb = kv0 + 4 * lh;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kv = kvb + 8 * (r >> 2) + (r & 3);
-          s0[r] = (kv < lim) ? s0[r] : kNegInf;
-        }
-      }
-      float mx = max3(s0[0], s0[1], s0[2]);
-#pragma unroll
-      for (int r = 3; r < 15; r += 2) mx = max3(mx, s0[r], s0[r + 1]);
-      mx = fmaxf(mx, s0[15]);
-      const float mxs = half_max(mx) * scale_log2;
-      const bool need = mxs > m + kLazyRescale;
-      if (wave_any(need)) {
-        const float alpha = need ? ((m == kNegInf) ? 0.f : fast_exp2(m - mxs)) : 1.f;
-        m = need ? mxs : m;
-        l *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-      }
-      const float nm = (m == kNegInf) ? 0.f : -m;
-      uint32_t pk[8];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s0[r], scale_log2, nm));
-        const float p1 = fast_exp2(__builtin_fmaf(s0[r + 1], scale_log2, nm));
-        l += p0 + p1;
-        pk[r >> 1] = TT::pack2(p0, p1);
-      }
-#pragma unroll
-      for (int t4 = 0; t4 < 2; ++t4) {
-        const u32x4_t bop = {pk[4 * t4 + 0], pk[4 * t4 + 1], pk[4 * t4 + 2], pk[4 * t4 + 3]};
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2_t lo = lds_read_tr16((const uint16_t*)(st_base + va[db] + 16 * t4 * L::RB));
-          const u32x2_t hi = lds_read_tr16((const uint16_t*)(st_base + va[db] + (16 * t4 + 8) * L::RB));
-          const u32x4_t aop = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = TT::mfma32(aop, bop, oacc[db]);
-        }
-      }
-    }
-    // tile t+1 must have landed (in-order count: only tile t+2's loads may be pending)
-    if (ahead)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * L::BPW));
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-  }
-
-  l = half_sum(l);
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
-  const auto rO = buffer_rsrc(O + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d = db * 32 + 8 * rg + 4 * lh;
-      const u32x2_t w = {TT::pack2(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv),
-                         TT::pack2(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv)};
-      buffer_store8(rO, (uint32_t)(qrow * D + d) * 2, w);
-    }
-  }
-  if (LSE != nullptr && lh == 0 && qrow < N_q) {
-    LSE[((int64_t)b * H_q + h) * N_q + qrow] = (l > 0.f) ? (m + log2f(l)) * kLn2 : kNegInf;
-  }
-}
-
-// Two-block form: each wavefront owns 64 query rows (two 32-row blocks), so
-// every K or V operand read from LDS feeds two MFMAs, halving LDS traffic per
-// FLOP; one wavefront per SIMD with the full register file. 32-key tiles are
-// streamed by direct loads into a 4-stage LDS ring, issued three tiles ahead.
-// The scores of tile t+1 are computed while tile t's exponentials run, so the
-// matrix cores and the vector ALUs work in the same stretch of code:
-//   iteration t: issue tile t+3; softmax statistics of S(t); S(t+1) = K(t+1) Q^T
-//   interleaved with P(t) = exp2(...); O += V(t) P(t); wait for tile t+2; barrier.
-constexpr int kW2Stages = 4;
-constexpr int kW2BM = 256;
-
-template <class TT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void prefill16_w2_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
-    float scale_log2, int nqb, int nbatch) {
-  using L = DL<D>;
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  static_assert(L::BPW >= 1 && L::BPW * 4 == L::BLK, "tile must split over 4 wavefronts");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kW2Stages * L::STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 31;
-  const int lh = lane >> 5;
-  const WorkItem wi = map_work(nqb, H_q, nbatch, CAUSAL);
-  if (!wi.valid) return;
-  const int qblk = wi.qblk, h = wi.h, b = wi.b;
-  const int hk = h / (H_q / H_kv);
-
-  const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
-  const uint32_t head_kv_bytes = (uint32_t)N_kv * D * 2;
-  const auto rQ = buffer_rsrc(Q + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
-
-  const int q0 = qblk * kW2BM + wave * 64;  // first row of this wavefront
-  const int off = N_kv - N_q;
-  int qrow[2], lim[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    qrow[j] = q0 + 32 * j + lr;
-    lim[j] = CAUSAL ? min(N_kv, max(qrow[j] + off + 1, 0)) : N_kv;
-  }
-  u32x4_t qreg[2][KS];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int st = 0; st < KS; ++st)
-      qreg[j][st] = buffer_load16(rQ, (uint32_t)(qrow[j] * D + 16 * st + 8 * lh) * 2);
-
-  int kv_end = N_kv;
-  if (CAUSAL) kv_end = min(N_kv, min(qblk * kW2BM + kW2BM - 1, N_q - 1) + off + 1);
-  const int ntiles = kv_end > 0 ? (kv_end + kDLBN - 1) / kDLBN : 0;
-  int wtiles = ntiles;
-  if (CAUSAL) wtiles = min(ntiles, max(0, (q0 + 63 + off + kDLBN) / kDLBN));
-
-  uint32_t kg_off[L::BPW], vg_off[L::BPW];
-#pragma unroll
-  for (int i = 0; i < L::BPW; ++i) {
-    const int p = (wave * L::BPW + i) * 64 + lane;
-    const int r = p / L::CPR, slot = p % L::CPR;
-    kg_off[i] = (uint32_t)(r * L::RB + ((slot ^ L::kswz(r)) * 16));
-    vg_off[i] = (uint32_t)(r * L::RB + ((slot ^ L::vswz(r)) * 16));
-  }
-  const auto dK = buffer_rsrc(K + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-  const auto dV = buffer_rsrc(V + ((int64_t)b * H_kv + hk) * (int64_t)N_kv * D, head_kv_bytes);
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  auto issue_tile = [&](int t) {
-    const int stage = t & (kW2Stages - 1);
-    const uint32_t g0 = (uint32_t)(t * kDLBN) * L::RB;
-#pragma unroll
-    for (int i = 0; i < L::BPW; ++i) {
-      const uint32_t kd = lds0 + stage * L::STAGE + (wave * L::BPW + i) * 1024;
-      dma_load16(dK, g0 + kg_off[i], kd);
-      dma_load16(dV, g0 + vg_off[i], kd + L::TILE);
-    }
-  };
-  int ka[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st) ka[st] = lr * L::RB + (((2 * st + lh) ^ L::kswz(lr)) * 16);
-  const int g = lane >> 4, gi = lane & 15;
-  const int vrow = 4 * (g >> 1) + (gi >> 2);
-  int va[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-    va[db] = L::TILE + vrow * L::RB + (((4 * db + 2 * (g & 1) + ((gi & 3) >> 1)) ^ L::vswz(vrow)) * 16) +
-             8 * (gi & 1);
-  auto gemm_s = [&](int t, f32x16_t (&sn)[2]) {
-    const uint8_t* base = smem + (t & (kW2Stages - 1)) * L::STAGE;
-    sn[0] = f32x16_t{0};
-    sn[1] = f32x16_t{0};
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      const u32x4_t a = *(const u32x4_t*)(base + ka[st]);
-      sn[0] = TT::mfma32(a, qreg[0][st], sn[0]);
-      sn[1] = TT::mfma32(a, qreg[1][st], sn[1]);
-    }
-  };
-
-  // prologue: tiles 0, 1, 2 requested; 0 and 1 landed
-  issue_tile(0);
-  issue_tile(1);
-  issue_tile(2);
-  if (ntiles > 2)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * L::BPW));
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-  vmem_wait_all();  // (the Q loads)
-  __syncthreads();
-
-  f32x16_t oacc[2][DB];
-  float m[2], l[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int i = 0; i < DB; ++i) oacc[j][i] = f32x16_t{0};
-    m[j] = kNegInf;
-    l[j] = 0.f;
-  }
-  f32x16_t sa[2], sb[2];
-  gemm_s(0, sa);
-
-  auto step = [&](int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
-    const bool ahead = t + 3 < ntiles;
-    if (ahead) issue_tile(t + 3);
-    if (t < wtiles) {
-      const int kv0 = t * kDLBN;
-      const bool need_mask = (kv0 + kDLBN > N_kv) || (CAUSAL && kv0 + kDLBN - 1 > q0 + off);
-      if (need_mask) {
-        const int kvb = kv0 + 4 * lh;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kv = kvb + 8 * (r >> 2) + (r & 3);
-            sc[j][r] = (kv < lim[j]) ? sc[j][r] : kNegInf;
-          }
-      }
-      float nm[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float mx = max3(sc[j][0], sc[j][1], sc[j][2]);
-#pragma unroll
-        for (int r = 3; r < 15; r += 2) mx = max3(mx, sc[j][r], sc[j][r + 1]);
-        mx = fmaxf(mx, sc[j][15]);
-        const float mxs = half_max(mx) * scale_log2;
-        const bool need = mxs > m[j] + kLazyRescale;
-        if (wave_any(need)) {
-          const float alpha = need ? ((m[j] == kNegInf) ? 0.f : fast_exp2(m[j] - mxs)) : 1.f;
-          m[j] = need ? mxs : m[j];
-          l[j] *= alpha;
-#pragma unroll
-          for (int i = 0; i < DB; ++i) oacc[j][i] *= alpha;
-        }
-        nm[j] = (m[j] == kNegInf) ? 0.f : -m[j];
-      }
-      // S(t+1) on the matrix cores while P(t) is formed
-      gemm_s(t + 1, sn);
-      uint32_t pk[2][8];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(sc[j][r], scale_log2, nm[j]));
-          const float p1 = fast_exp2(__builtin_fmaf(sc[j][r + 1], scale_log2, nm[j]));
-          l[j] += p0 + p1;
-          pk[j][r >> 1] = TT::pack2(p0, p1);
-        }
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // K operand read
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two score MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x002, 80 / KS, 0);  // exp / convert / sum
-      }
-      // O += V(t) P(t): each transposed V operand feeds both query blocks
-      const uint8_t* base = smem + (t & (kW2Stages - 1)) * L::STAGE;
-#pragma unroll
-      for (int t4 = 0; t4 < 2; ++t4) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2_t lo = lds_read_tr16((const uint16_t*)(base + va[db] + 16 * t4 * L::RB));
-          const u32x2_t hi = lds_read_tr16((const uint16_t*)(base + va[db] + (16 * t4 + 8) * L::RB));
-          const u32x4_t aop = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const u32x4_t bop = {pk[j][4 * t4 + 0], pk[j][4 * t4 + 1], pk[j][4 * t4 + 2], pk[j][4 * t4 + 3]};
-            oacc[j][db] = TT::mfma32(aop, bop, oacc[j][db]);
-          }
-        }
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * DB - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    }
-    // tile t+2 must have landed (only tile t+3's loads may still be pending)
-    if (ahead)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * L::BPW));
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, sa, sb);
-    if (t + 1 < ntiles) step(t + 1, sb, sa);
-  }
-
-  const auto rO = buffer_rsrc(O + ((int64_t)b * H_q + h) * (int64_t)N_q * D, head_q_bytes);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float lt = half_sum(l[j]);
-    const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d = db * 32 + 8 * rg + 4 * lh;
-        const u32x2_t w = {TT::pack2(oacc[j][db][4 * rg + 0] * inv, oacc[j][db][4 * rg + 1] * inv),
-                           TT::pack2(oacc[j][db][4 * rg + 2] * inv, oacc[j][db][4 * rg + 3] * inv)};
-        buffer_store8(rO, (uint32_t)(qrow[j] * D + d) * 2, w);
-      }
-    }
-    if (LSE != nullptr && lh == 0 && qrow[j] < N_q) {
-      LSE[((int64_t)b * H_q + h) * N_q + qrow[j]] = (lt > 0.f) ? (m[j] + log2f(lt)) * kLn2 : kNegInf;
-    }
-  }
-}
 
 constexpr int kRingStages = 3;
 
@@ -1554,8 +466,8 @@ __device__ __forceinline__ void lds_barrier() {
 // tile's time to arrive. They are issued after tile g's V operands have been
 // read: the compiler makes a transposing LDS read wait for every direct load in
 // flight, and at that point only tile g+1's loads are, which are due anyway.
-// LDS rows are unpadded, their 16-byte chunks XOR-swizzled as in the
-// direct-load form. One 32-row query block per wavefront; otherwise (work
+// LDS rows are unpadded, their 16-byte chunks XOR-swizzled (RingLds). One
+// 32-row query block per wavefront; otherwise (work
 // items, masking, causal skipping, the online softmax) as the default kernel.
 template <class TT, int D, bool CAUSAL, int NW, bool PERSIST>
 __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<1, D>::kWaves)) void prefill16_ring_kernel(
@@ -1563,7 +475,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<1, D>::kWaves)) void pr
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
     float scale_log2, int nqb, int nbatch, const int* __restrict__ kv_lens = nullptr,
     int row_period = 0) {
-  using L = DL<D, kBN>;
+  using L = RingLds<D>;
   constexpr int KS = D / 16;   // k-steps of the score MFMA
   constexpr int DB = D / 32;   // 32-wide blocks of the output
   constexpr int BM = NW * 32;  // query rows per workgroup
@@ -2067,122 +979,25 @@ hipError_t launch16q(const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class TT, int D>
-hipError_t launch16p(const PrefillArgs& a, hipStream_t st) {
-  const int nqb = (a.N_q + kBM - 1) / kBM;
-  dim3 grid(xcd_grid((int64_t)nqb * a.H_q * a.B));
-  const float sl2 = a.scale * kLog2e;
-  auto q = (const uint16_t*)a.q;
-  auto k = (const uint16_t*)a.k;
-  auto v = (const uint16_t*)a.v;
-  auto o = (uint16_t*)a.o;
-  if (a.causal)
-    hipLaunchKernelGGL((prefill16_pipe_kernel<TT, D, true>), grid, dim3(kThreads), 0, st, q, k, v, o,
-                       a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
-  else
-    hipLaunchKernelGGL((prefill16_pipe_kernel<TT, D, false>), grid, dim3(kThreads), 0, st, q, k, v, o,
-                       a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
-  return hipGetLastError();
-}
-
-template <class TT, int D>
-hipError_t launch16pp(const PrefillArgs& a, hipStream_t st) {
-  const int nqb = (a.N_q + kPPBM - 1) / kPPBM;
-  dim3 grid(xcd_grid((int64_t)nqb * a.H_q * a.B));
-  const float sl2 = a.scale * kLog2e;
-  auto q = (const uint16_t*)a.q;
-  auto k = (const uint16_t*)a.k;
-  auto v = (const uint16_t*)a.v;
-  auto o = (uint16_t*)a.o;
-  if (a.causal)
-    hipLaunchKernelGGL((prefill16_pp_kernel<TT, D, true, (D == 64)>), grid, dim3(kPPThreads), 0, st, q, k, v,
-                       o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
-  else
-    hipLaunchKernelGGL((prefill16_pp_kernel<TT, D, false, (D == 64)>), grid, dim3(kPPThreads), 0, st, q, k, v,
-                       o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
-  return hipGetLastError();
-}
-
-template <class TT, int D>
-hipError_t launch16dl(const PrefillArgs& a, hipStream_t st) {
-  const int nqb = (a.N_q + kBM - 1) / kBM;
-  dim3 grid(xcd_grid((int64_t)nqb * a.H_q * a.B));
-  const float sl2 = a.scale * kLog2e;
-  auto q = (const uint16_t*)a.q;
-  auto k = (const uint16_t*)a.k;
-  auto v = (const uint16_t*)a.v;
-  auto o = (uint16_t*)a.o;
-  if (a.causal)
-    hipLaunchKernelGGL((prefill16_dl_kernel<TT, D, true>), grid, dim3(kThreads), 0, st, q, k, v, o,
-                       a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
-  else
-    hipLaunchKernelGGL((prefill16_dl_kernel<TT, D, false>), grid, dim3(kThreads), 0, st, q, k, v, o,
-                       a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
-  return hipGetLastError();
-}
-
-template <class TT, int D>
-hipError_t launch16w2(const PrefillArgs& a, hipStream_t st) {
-  const int nqb = (a.N_q + kW2BM - 1) / kW2BM;
-  dim3 grid(xcd_grid((int64_t)nqb * a.H_q * a.B));
-  const float sl2 = a.scale * kLog2e;
-  auto q = (const uint16_t*)a.q;
-  auto k = (const uint16_t*)a.k;
-  auto v = (const uint16_t*)a.v;
-  auto o = (uint16_t*)a.o;
-  if (a.causal)
-    hipLaunchKernelGGL((prefill16_w2_kernel<TT, D, true>), grid, dim3(kThreads), 0, st, q, k, v, o,
-                       a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
-  else
-    hipLaunchKernelGGL((prefill16_w2_kernel<TT, D, false>), grid, dim3(kThreads), 0, st, q, k, v, o,
-                       a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
-  return hipGetLastError();
-}
-
 // Kernel form for 16-bit inputs: one 32-row query block per wavefront, 8
 // wavefronts (256 rows) per workgroup for d = 128 and 4 (128 rows) for d = 64,
 // where the smaller register footprint buys a third resident wavefront per
-// SIMD instead. ATTN_PREFILL_VARIANT selects alternative forms (tuning only):
-// 1 = 4 wavefronts, 2 = two query blocks per wavefront, 3 = software-pipelined
-// scores, 4 = two ping-ponging wavefront groups, 5 = direct-load 3-stage ring,
-// 6 = two query blocks with a direct-load ring, 7 = 8 wavefronts, 8 = the
-// default kernel with one work item per workgroup instead of a persistent grid,
-// 9 = two wavefront groups skewed by half a tile, 10 = the default kernel's ring
-// form (direct loads), 11 = its register-staged form.
-template <class TT, int D>
-hipError_t launch16skew(const PrefillArgs& a, hipStream_t st) {
-  const int nqb = (a.N_q + 255) / 256;
-  dim3 grid(xcd_grid((int64_t)nqb * a.H_q * a.B));
-  const float sl2 = a.scale * kLog2e;
-  auto q = (const uint16_t*)a.q;
-  auto k = (const uint16_t*)a.k;
-  auto v = (const uint16_t*)a.v;
-  auto o = (uint16_t*)a.o;
-  if (a.causal)
-    hipLaunchKernelGGL((prefill16_skew_kernel<TT, D, true>), grid, dim3(512), 0, st, q, k, v, o, a.lse,
-                       a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
-  else
-    hipLaunchKernelGGL((prefill16_skew_kernel<TT, D, false>), grid, dim3(512), 0, st, q, k, v, o, a.lse,
-                       a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
-  return hipGetLastError();
-}
-
+// SIMD instead. ATTN_PREFILL_VARIANT selects alternative forms (tuning and
+// testing only): 1 = 4 wavefronts per workgroup, one work item each; 2 = two
+// query blocks per wavefront; 3 = the default wavefront count with one work
+// item per workgroup instead of a persistent grid; 4 = the ring form (direct
+// loads) at either d; 5 = the register-staged form at either d.
 template <class TT, int D>
 hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
+  constexpr int NW = (D == 128) ? 8 : 4;
   const char* env = getenv("ATTN_PREFILL_VARIANT");
   const int variant = env ? atoi(env) : 0;
-  if (variant == 2) return launch16q<TT, D, 2>(a, st);
-  if (variant == 3) return launch16p<TT, D>(a, st);
-  if (variant == 4) return launch16pp<TT, D>(a, st);
-  if (variant == 5) return launch16dl<TT, D>(a, st);
   if (variant == 1) return launch16q<TT, D, 1, 4>(a, st);
-  if (variant == 6) return launch16w2<TT, D>(a, st);
-  if (variant == 7) return launch16q<TT, D, 1, 8>(a, st);
-  if (variant == 8) return launch16q<TT, D, 1, (D == 128 ? 8 : 4)>(a, st);
-  if (variant == 9) return launch16skew<TT, D>(a, st);
-  if (variant == 10) return launch16pers<TT, D, (D == 128 ? 8 : 4), true>(a, st);
-  if (variant == 11) return launch16pers<TT, D, (D == 128 ? 8 : 4), false>(a, st);
-  return launch16pers<TT, D, (D == 128 ? 8 : 4), kRingDefault<D>>(a, st);
+  if (variant == 2) return launch16q<TT, D, 2>(a, st);
+  if (variant == 3) return launch16q<TT, D, 1, NW>(a, st);
+  if (variant == 4) return launch16pers<TT, D, NW, true>(a, st);
+  if (variant == 5) return launch16pers<TT, D, NW, false>(a, st);
+  return launch16pers<TT, D, NW, kRingDefault<D>>(a, st);
 }
 
 template <int D>
@@ -2211,8 +1026,8 @@ hipError_t launch_prefill_rows(const PrefillArgs& a, const int* kv_lens, int row
                                hipStream_t st) {
   const char* env = getenv("ATTN_PREFILL_VARIANT");
   const int variant = env ? atoi(env) : 0;
-  if (variant == 10 || variant == 11) {  // tuning and testing: force the ring or the staged form
-    const bool ring = variant == 10;
+  if (variant == 4 || variant == 5) {  // tuning and testing: force the ring or the staged form
+    const bool ring = variant == 4;
     if (a.dtype == kDtypeBF16)
       return a.d == 64 ? (ring ? launch16pers<BF16, 64, 4, true>(a, st, kv_lens, row_period)
                                : launch16pers<BF16, 64, 4, false>(a, st, kv_lens, row_period))

@@ -162,7 +162,7 @@ def test_prefill_full_size_sampled(cid):
 MANY_ITEMS = [(2, 64, 64, 700, 700, 128), (4, 64, 16, 500, 500, 64), (1, 48, 8, 1100, 2000, 128)]
 
 
-@pytest.mark.parametrize("form", [None, "10", "11"], ids=["default", "ring", "staged"])
+@pytest.mark.parametrize("form", [None, "4", "5"], ids=["default", "ring", "staged"])
 @pytest.mark.parametrize("slots", [None, "16", "8"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", MANY_ITEMS, ids=lambda s: "x".join(map(str, s)))
@@ -177,7 +177,7 @@ def test_prefill_persistent_grid_many_items(shape, causal, slots, form, monkeypa
     _run_small(*shape, "bf16", causal, seed=zlib.crc32(repr((shape, causal)).encode()) % 10000)
 
 
-@pytest.mark.parametrize("variant", ["1", "2", "3", "4", "5", "6", "7", "8", "9", "10", "11"])
+@pytest.mark.parametrize("variant", ["1", "2", "3", "4", "5"])
 def test_prefill_variants_match_oracle(variant, monkeypatch):
     """Every alternative kernel behind ATTN_PREFILL_VARIANT (tuning only) meets
     the same bar as the default."""
