@@ -15,7 +15,8 @@ to bf16/fp16 on the device side are both exact):
   rounded RNE to the storage dtype (bf16: integer rounding of the fp32 bits;
   fp16: numpy's float16 cast, which is RNE; fp32: unchanged)
 
-tensor ids: Q=0, K=1, V=2; ragged decode lengths use SeedSequence([31, cfg, 3]).
+tensor ids: Q=0, K=1, V=2, dO=4 (the output gradient of backward workloads);
+ragged decode lengths use SeedSequence([31, cfg, 3]).
 Paged-cache block tables are a seeded permutation of the pool's blocks,
 SeedSequence([31, 2000, seed]). FP8 caches are E4M3 codes of sigma * N(0, 1)
 divided by a per-tensor scale, SeedSequence([31, 3000, seed]), rounded by

@@ -4,7 +4,9 @@ import os
 
 import numpy as np
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2}
+# "do" is the output gradient of the backward workloads (shaped like Q); 3 is
+# taken by the ragged decode lengths
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 4}
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -43,7 +45,7 @@ def _rng(*key: int) -> np.random.Generator:
 
 def slice_values(cid: int, tensor: str, b: int, h: int, n: int, d: int, sigma: float,
                  dtype: str) -> np.ndarray:
-    """One [n, d] slice (batch b, head h) of tensor 'q' | 'k' | 'v' as exact float32 values."""
+    """One [n, d] slice (batch b, head h) of tensor 'q' | 'k' | 'v' | 'do' as exact float32 values."""
     x = _rng(31, cid, TENSOR_IDS[tensor], b, h).standard_normal((n, d), dtype=np.float32)
     if sigma != 1.0:
         x *= np.float32(sigma)
@@ -52,8 +54,8 @@ def slice_values(cid: int, tensor: str, b: int, h: int, n: int, d: int, sigma: f
 
 def tensor_values(cfg, tensor: str, threads: int | None = None) -> np.ndarray:
     """A whole [B, H, N, d] tensor of a config as exact float32 values (threaded per slice)."""
-    H = cfg.H_q if tensor == "q" else cfg.H_kv
-    N = cfg.N_q if tensor == "q" else cfg.N_kv
+    H = cfg.H_q if tensor in ("q", "do") else cfg.H_kv
+    N = cfg.N_q if tensor in ("q", "do") else cfg.N_kv
     out = np.empty((cfg.B, H, N, cfg.d), dtype=np.float32)
 
     def fill(bh):

@@ -79,8 +79,8 @@ def decode_kv_bytes(cfg, lens) -> int:
 def make_device_tensor(cfg, name, torch, threads=16):
     import attn_inputs as A
     dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
-    H = cfg.H_q if name == "q" else cfg.H_kv
-    N = cfg.N_q if name == "q" else cfg.N_kv
+    H = cfg.H_q if name in ("q", "do") else cfg.H_kv
+    N = cfg.N_q if name in ("q", "do") else cfg.N_kv
     t = torch.empty((cfg.B, H, N, cfg.d), dtype=dt, device="cuda")
 
     def gen(bh):
@@ -234,7 +234,7 @@ def bench_backward(cfg, steps, warmup, torch, E):
     k = make_device_tensor(cfg, "k", torch)
     v = make_device_tensor(cfg, "v", torch)
     o, lse = E.attn_prefill_fwd(q, k, v, causal=cfg.causal, scale=cfg.scale, return_lse=True)
-    do = torch.randn_like(q)
+    do = make_device_tensor(cfg, "do", torch)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(E.attn_backward_workspace_size(cfg.B, cfg.H_q, cfg.H_kv, cfg.N_q, cfg.N_kv, cfg.d,
                                                     q.dtype), dtype=torch.uint8, device="cuda")

@@ -27,8 +27,8 @@ def device_tensor(cfg, name: str, keep=(), device="cuda"):
     """Fill a [B, H, N, d] device tensor of config `cfg` slice by slice.
 
     Returns (tensor, {(b, h): float32 host slice for (b, h) in keep})."""
-    H = cfg.H_q if name == "q" else cfg.H_kv
-    N = cfg.N_q if name == "q" else cfg.N_kv
+    H = cfg.H_q if name in ("q", "do") else cfg.H_kv
+    N = cfg.N_q if name in ("q", "do") else cfg.N_kv
     t = torch.empty((cfg.B, H, N, cfg.d), dtype=TORCH_DT[cfg.dtype], device=device)
     keep = set(keep)
     kept = {}

@@ -44,3 +44,13 @@ def test_config_table():
     # multi-token decode shares config 5's caches (same seeds), 4 queries per head
     assert (c[7].cid, c[7].N_q, c[7].N_kv, c[7].causal, c[7].G) == (5, 4, 32768, True, 8)
     assert (c[8].cid, c[8].N_q, c[8].N_kv, c[8].causal) == (5, 64, 32768, True)
+
+
+def test_output_gradient_has_its_own_stream():
+    """dO (tensor id 4) is shaped like Q and drawn from its own seed stream."""
+    cfg = A.CONFIGS[2]
+    q = A.slice_values(cfg.cid, "q", 1, 3, 64, cfg.d, cfg.sigma, cfg.dtype)
+    g = A.slice_values(cfg.cid, "do", 1, 3, 64, cfg.d, cfg.sigma, cfg.dtype)
+    assert g.shape == q.shape and not np.array_equal(g, q)
+    assert np.array_equal(g, A.slice_values(cfg.cid, "do", 1, 3, 64, cfg.d, cfg.sigma, cfg.dtype))
+    assert np.array_equal(g, A.bf16_round(g))
