@@ -186,9 +186,18 @@ def bench_decode_paged(cfg, steps, warmup, torch, E, cache, block_size=16):
                                 causal=cfg.causal, workspace=ws)
 
     ms, wall = time_launches(call, steps, warmup, torch)
-    # the same logical cache through the contiguous path gives the same bits
-    oc = E.attn_decode_fwd(q, k, v, kv_lens=lens_d, scale=cfg.scale, causal=cfg.causal)
-    torch.cuda.synchronize()
+    # the same logical cache through the contiguous path, held to the paged
+    # path's 2048-key splits, gives the same bits
+    prev = os.environ.get("ATTN_DECODE_CHUNK")
+    os.environ["ATTN_DECODE_CHUNK"] = "2048"
+    try:
+        oc = E.attn_decode_fwd(q, k, v, kv_lens=lens_d, scale=cfg.scale, causal=cfg.causal)
+        torch.cuda.synchronize()
+    finally:
+        if prev is None:
+            del os.environ["ATTN_DECODE_CHUNK"]
+        else:
+            os.environ["ATTN_DECODE_CHUNK"] = prev
     same = bool(torch.equal(o, oc))
     nbytes = decode_kv_bytes(cfg, lens)
     gbs = nbytes / (ms * 1e-3) / 1e9

@@ -212,7 +212,7 @@ int decode_launch(const void* q, const void* k, const void* v, size_t kv_bytes, 
     }
   }
   attn::DecodeArgs a{q, k, v, kv_lens, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale, dtype,
-                     plan.chunk, plan.splits, g_dev_cus[dev], ws,
+                     plan.chunk, plan.splits, plan.chunk_cap, g_dev_cus[dev], ws,
                      ws + (size_t)B * H_q * N_q * plan.splits * d,
                      paged ? table : nullptr, max_blocks, paged ? log2_of(block_size) : 0,
                      num_blocks, kv_fp8 ? 1 : 0, k_scale, v_scale};

@@ -35,8 +35,9 @@ struct DecodeArgs {
   int causal;
   float scale;
   int dtype;
-  int chunk;   // keys per split
-  int splits;  // splits per (request, KV head), = ceil(N_kv / chunk)
+  int chunk;      // keys per split (the plan's; sizes the workspace)
+  int splits;     // splits per (request, KV head), = ceil(N_kv / chunk)
+  int chunk_cap;  // the kernels may raise the split up to this many keys (>= chunk)
   int num_cus; // compute units of the device (sizes the persistent grid)
   float* part_u;   // [B, H_q, N_q, splits, d] un-normalised partial outputs
   float* part_ml;  // [B, H_q, N_q, splits, 2] partial (max in log2 units, denominator)
@@ -55,6 +56,7 @@ struct DecodeArgs {
 struct DecodePlan {
   int chunk;
   int splits;
+  int chunk_cap;  // largest split the kernels may choose from the actual lengths
   size_t workspace_bytes;
 };
 DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool paged);

@@ -67,9 +67,57 @@ struct SplitParams {
   const int* kv_lens;
   float* part_u;
   float* part_ml;
-  int B, H_q, H_kv, N_q, N_kv, causal, splits, chunk;
+  int B, H_q, H_kv, N_q, N_kv, causal, splits, chunk, chunk_cap;
   float scale_log2;  // softmax scale * log2(e) (times the K dequantisation scale for FP8)
 };
+
+// Keys per work unit, chosen on the device from the requests' actual lengths.
+// The host plan's chunk sizes the workspace (ceil(N_kv / chunk) partials per
+// query row); a larger chunk never needs more. Starting from the batch's keys
+// per wavefront, the split grows (up to cap) until the units of the whole
+// batch number at most one per wavefront of the grid: every wavefront still
+// gets a unit when the lengths allow, and the per-unit costs (start-up, the
+// partial results and their merge) are paid as few times as possible. Each
+// lane reads the lengths of requests lane, lane + 64, ... at once, and the
+// sums are wavefront reductions; the unit counts use a float reciprocal (a
+// heuristic needs no exact division). The result is a pure function of the
+// arguments: the merge kernel evaluates it on the same inputs as the split
+// kernel. Above kAdaptMaxB requests the plan's chunk is kept. Called by all
+// 64 lanes of a wavefront.
+constexpr int kAdaptMaxB = 1024;
+__device__ int unit_chunk(const int* __restrict__ kv_lens, int B, int N_kv, int chunk, int cap,
+                          int HG, int nwaves) {
+  if (cap <= chunk || B > kAdaptMaxB || nwaves <= 0) return chunk;
+  constexpr int PER = kAdaptMaxB / 64;
+  const int lane = (int)threadIdx.x & 63;
+  float len[PER];
+  float total = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int b = lane + 64 * i;
+    const int n = b < B ? (kv_lens ? kv_lens[b] : N_kv) : 0;
+    len[i] = (float)min(max(n, 0), N_kv);
+    total += len[i];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) total += __shfl_xor(total, o);
+  if (total == 0.f) return chunk;
+  const float cf = fminf(ceilf(total * (float)HG / (float)nwaves), (float)cap);
+  int c = ((int)cf + kStepKeys - 1) / kStepKeys * kStepKeys;
+  c = c < chunk ? chunk : (c > cap ? cap : c);
+  for (int it = 0; it < 32 && c < cap; ++it) {
+    const float rc = 1.f / (float)c;
+    float units = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) units += ceilf(len[i] * rc);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) units += __shfl_xor(units, o);
+    if (units * (float)HG <= (float)nwaves) break;
+    const int step = (c / 16 + kStepKeys - 1) / kStepKeys * kStepKeys;
+    c = c + step > cap ? cap : c + step;
+  }
+  return __builtin_amdgcn_readfirstlane(c);
+}
 
 // Four FP8 E4M3 codes (one dword) to four bf16 values (two dwords), exactly:
 // every E4M3 value is a bf16 value.
@@ -88,8 +136,8 @@ __device__ __forceinline__ u32x2_t fp8x4_to_bf16(uint32_t w) {
 // into LDS (V); the dequantisation scales are applied to the score scale and,
 // in the merge, to the output.
 template <class TT, int D, int NG, bool PAGED, bool FP8>
-__device__ __forceinline__ void wave_unit(const SplitParams& P, int b, int hk, int qg, int split,
-                                          int len, uint16_t* sV) {
+__device__ __forceinline__ void wave_unit(const SplitParams& P, int chunk, int b, int hk, int qg,
+                                          int split, int len, uint16_t* sV) {
   constexpr int VST = DecLds<D>::VST;
   constexpr int KS = D / 32;        // k-steps of the score MFMA
   constexpr int DB = D / 16;        // 16-wide output blocks
@@ -104,8 +152,8 @@ __device__ __forceinline__ void wave_unit(const SplitParams& P, int b, int hk, i
   const int g = lane >> 4;     // 16-lane group
   const int H_kv = P.H_kv, N_q = P.N_q;
   const int G = P.H_q / H_kv;
-  const int wbeg = split * P.chunk;
-  const int wend = min(wbeg + P.chunk, len);
+  const int wbeg = split * chunk;
+  const int wend = min(wbeg + chunk, len);
   const int nsteps = (wend - wbeg + kWaveKeys - 1) / kWaveKeys;
   const float scale_log2 = P.scale_log2;
 
@@ -346,7 +394,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(const Split
   const int ngroups = (G * P.N_q + NG * kQCols - 1) / (NG * kQCols);  // units of NG column groups
   const int HG = P.H_kv * ngroups;
   const int nw = (int)gridDim.x * 4;
-  const int B = P.B, chunk = P.chunk;
+  const int B = P.B;
+  const int chunk = unit_chunk(P.kv_lens, B, P.N_kv, P.chunk, P.chunk_cap, HG, nw);
   auto len_of = [&](int b) {
     const int n = P.kv_lens ? P.kv_lens[b] : P.N_kv;
     return min(max(n, 0), P.N_kv);
@@ -366,7 +415,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(const Split
       }
     }
     if (cb >= B) break;
-    wave_unit<TT, D, NG, PAGED, FP8>(P, cb, hg / ngroups, hg - (hg / ngroups) * ngroups, c - cstart, lb, sV);
+    wave_unit<TT, D, NG, PAGED, FP8>(P, chunk, cb, hg / ngroups, hg - (hg / ngroups) * ngroups,
+                                     c - cstart, lb, sV);
   }
 }
 
@@ -379,7 +429,8 @@ template <class TT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part_u, const float* __restrict__ part_ml,
     const int* __restrict__ kv_lens, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int rows_per_b, int N_kv, int splits, int chunk, int BH, float out_scale) {
+    int rows_per_b, int N_kv, int splits, int chunk, int chunk_cap, int HG, int nwaves, int BH,
+    float out_scale) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int PER = D / 64;  // columns per lane
   const int lane = threadIdx.x & 63;
@@ -388,7 +439,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int b = bh / rows_per_b;
   int len = kv_lens ? kv_lens[b] : N_kv;
   len = min(max(len, 0), N_kv);
-  const int ns = (len + chunk - 1) / chunk;
+  // the split kernel's units: the same function of the same inputs
+  const int ce = unit_chunk(kv_lens, BH / rows_per_b, N_kv, chunk, chunk_cap, HG, nwaves);
+  const int ns = (len + ce - 1) / ce;
   const int64_t row0 = (int64_t)bh * splits;
   float M = kNegInf;
   for (int s = lane; s < ns; s += 64) M = fmaxf(M, part_ml[(row0 + s) * 2]);
@@ -461,6 +514,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   P.causal = a.causal;
   P.splits = a.splits;
   P.chunk = a.chunk;
+  P.chunk_cap = a.chunk_cap;
   P.scale_log2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
   if (a.block_table != nullptr)
     hipLaunchKernelGGL((decode_split_kernel<TT, D, NG, OCC, true, FP8>), grid, dim3(kThreads), 0, st, P);
@@ -471,7 +525,8 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   const int BH = a.B * a.H_q * a.N_q;
   hipLaunchKernelGGL((decode_merge_kernel<TT, D>), dim3((BH + 3) / 4), dim3(256), 0, st, a.part_u,
                      a.part_ml, a.kv_lens, (uint16_t*)a.o, a.lse, a.H_q * a.N_q, a.N_kv, a.splits,
-                     a.chunk, BH, FP8 ? a.v_scale : 1.f);
+                     a.chunk, a.chunk_cap, a.H_kv * ngroups, (int)grid.x * 4, BH,
+                     FP8 ? a.v_scale : 1.f);
   return hipGetLastError();
 }
 
@@ -505,16 +560,23 @@ DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool 
   chunk = ((chunk + kWaveKeys * 4 - 1) / (kWaveKeys * 4)) * (kWaveKeys * 4);
   if (chunk < 128) chunk = 128;
   if (chunk > 2048) chunk = 2048;
-  // tuning override (keys per split, rounded up to a multiple of 128; at most
-  // 2048 for paged caches, whose chunks keep their block-table entries in one
-  // register pair per lane)
+  // The kernels may raise the split on the device, from the actual lengths
+  // (unit_chunk), up to one chunk per request for contiguous caches; paged
+  // caches keep at most 2048 keys per chunk, whose block-table entries sit in
+  // one register pair per lane.
+  int64_t cap = paged ? 2048 : ((int64_t)N_kv + kStepKeys - 1) / kStepKeys * kStepKeys;
+  // tuning override (keys per split, rounded up to a multiple of 128, used as
+  // given: no raise on the device)
   if (const char* e = getenv("ATTN_DECODE_CHUNK")) {
     const long v = strtol(e, nullptr, 10);
     if (v > 0 && v <= (1L << 24)) chunk = ((v + kStepKeys - 1) / kStepKeys) * kStepKeys;
     if (paged && chunk > 2048) chunk = 2048;
+    cap = chunk;
   }
+  if (cap < chunk) cap = chunk;
   DecodePlan p;
   p.chunk = (int)chunk;
+  p.chunk_cap = (int)cap;
   p.splits = N_kv > 0 ? (int)((N_kv + chunk - 1) / chunk) : 1;
   p.workspace_bytes = (size_t)B * H_q * N_q * p.splits * (size_t)(d + 2) * sizeof(float);
   return p;

@@ -201,3 +201,13 @@ def test_decode_rows_mode_both_kernel_forms(case, form, monkeypatch):
     B, Hq, Hkv, Nkv, d, Nq, lens = case
     _decode_case(B, Hq, Hkv, Nkv, d, "bf16", lens,
                  seed=zlib.crc32(repr((case, form)).encode()) % 10000, Nq=Nq, causal=True)
+
+
+@pytest.mark.parametrize("ragged", [False, True], ids=["uniform", "ragged"])
+def test_decode_device_chosen_split_matches_oracle(ragged):
+    """Enough (request, KV head) pairs that the grid is full: the kernels then
+    raise the split size on the device from the actual lengths (to about one
+    unit per wavefront), and the merge must find the same splits."""
+    lens = np.random.default_rng(7).integers(1, 8193, size=40) if ragged else None
+    _decode_case(40, 32, 4, 8192, 64, "bf16", lens, seed=96)
+    _decode_case(40, 32, 4, 8192, 64, "bf16", lens, seed=97, Nq=3, causal=True)

@@ -72,7 +72,7 @@ def test_decode_multi_token_full_size_sampled(c5_cache, cid):
     print(f"{cfg.name}: worst sampled max|err| = {worst:.3e}", flush=True)
 
 
-def test_paged_decode_config5_full_size(c5_cache):
+def test_paged_decode_config5_full_size(c5_cache, monkeypatch):
     """Config 5 through a paged cache of 16-position blocks scattered over a
     pool in a seeded order (the benchmark's layout): the same bits as the
     contiguous path on every head, and the oracle on the sampled ones."""
@@ -93,6 +93,9 @@ def test_paged_decode_config5_full_size(c5_cache):
     lens_d = torch.from_numpy(lens).cuda()
     o, lse = E.attn_decode_paged_fwd(q, kp, vp, torch.from_numpy(table).cuda(), kv_lens=lens_d,
                                      scale=cfg.scale, return_lse=True)
+    # paged caches keep 2048-key splits; the contiguous path, held to the same
+    # split, must give the same bits
+    monkeypatch.setenv("ATTN_DECODE_CHUNK", "2048")
     oc, lc = E.attn_decode_fwd(q, k, v, kv_lens=lens_d, scale=cfg.scale, return_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(o, oc) and torch.equal(lse, lc)

@@ -80,10 +80,12 @@ def test_paged_decode_never_reads_unreferenced_memory(bs):
 
 
 @pytest.mark.parametrize("bs", [16, 128])
-def test_paged_equals_contiguous_bit_for_bit(bs):
+def test_paged_equals_contiguous_bit_for_bit(bs, monkeypatch):
     """A contiguous cache laid out as pool blocks (in a shuffled order) gives the
     same bits through the paged path as through the contiguous path: the
-    arithmetic is the same, only the addressing differs."""
+    arithmetic is the same, only the addressing differs. (Both held to one split
+    size: the two paths may otherwise choose different ones.)"""
+    monkeypatch.setenv("ATTN_DECODE_CHUNK", "512")
     B, Hq, Hkv, d, N = 3, 16, 2, 128, 4096
     _announce(f"paged vs contiguous bs={bs}")
     q = to_device(A.random_tensor((B, Hq, 2, d), 61, "bf16"), "bf16")
