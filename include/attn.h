@@ -73,9 +73,11 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * Bytes of device workspace attn_decode_fwd needs for these sizes (0 if the
- * sizes are invalid or N_q is outside [1, 64]). The split of the KV sequence is
- * a pure function of (B, H_q, H_kv, N_q, N_kv, d), so the same sizes always
- * need the same workspace.
+ * sizes are invalid or N_q is outside [1, 64]). The size is a pure function of
+ * (B, H_q, H_kv, N_q, N_kv, d): it holds the partials of the finest split of
+ * the KV sequence the call may use (the kernels may choose a coarser split on
+ * the device from kv_lens, which needs no more), so the same sizes always need
+ * the same workspace.
  */
 size_t attn_decode_workspace_size(int B, int H_q, int H_kv, int N_q, int N_kv, int d, int dtype);
 
