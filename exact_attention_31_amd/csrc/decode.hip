@@ -494,9 +494,11 @@ template <class TT, int D, int NG, int OCC, bool FP8>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   const int G = a.H_q / a.H_kv;
   const int ngroups = (G * a.N_q + NG * kQCols - 1) / (NG * kQCols);
-  // OCC resident workgroups per compute unit; never more than the units there can be
+  // OCC resident workgroups per compute unit (one for FP8 caches, whose units
+  // carry half the bytes: measured faster with half the wavefronts and twice
+  // the keys per unit); never more than the units there can be
   const int64_t units = (int64_t)a.B * a.H_kv * ngroups * a.splits;
-  const int64_t slots = (int64_t)OCC * (a.num_cus > 0 ? a.num_cus : 256);  // workgroups of 4 wavefronts
+  const int64_t slots = (int64_t)(FP8 ? 1 : OCC) * (a.num_cus > 0 ? a.num_cus : 256);
   const int64_t wgs = (units + 3) / 4;
   dim3 grid((unsigned)(wgs < slots ? wgs : slots));
   SplitParams P;
