@@ -73,17 +73,18 @@ struct SplitParams {
 
 // Keys per work unit, chosen on the device from the requests' actual lengths.
 // The host plan's chunk sizes the workspace (ceil(N_kv / chunk) partials per
-// query row); a larger chunk never needs more. Starting from the batch's keys
-// per wavefront, the split grows (up to cap) until the units of the whole
-// batch number at most one per wavefront of the grid: every wavefront still
-// gets a unit when the lengths allow, and the per-unit costs (start-up, the
-// partial results and their merge) are paid as few times as possible. Each
-// lane reads the lengths of requests lane, lane + 64, ... at once, and the
-// sums are wavefront reductions; the unit counts use a float reciprocal (a
-// heuristic needs no exact division). The result is a pure function of the
-// arguments: the merge kernel evaluates it on the same inputs as the split
-// kernel. Above kAdaptMaxB requests the plan's chunk is kept. Called by all
-// 64 lanes of a wavefront.
+// query row); a larger chunk never needs more. When every request has the
+// same length, the split grows from the batch's keys per wavefront (up to
+// cap) until the units of the whole batch number at most one per wavefront of
+// the grid: every wavefront still gets a unit, and the per-unit costs
+// (start-up, the partial results and their merge) are paid as few times as
+// possible. Unequal lengths keep the plan's finer split, which balances them
+// better. Each lane reads the lengths of requests lane, lane + 64, ... at
+// once, and the sums are wavefront reductions; the unit counts use a float
+// reciprocal (a heuristic needs no exact division). The result is a pure
+// function of the arguments: the merge kernel evaluates it on the same inputs
+// as the split kernel. Above kAdaptMaxB requests the plan's chunk is kept.
+// Called by all 64 lanes of a wavefront.
 constexpr int kAdaptMaxB = 1024;
 __device__ int unit_chunk(const int* __restrict__ kv_lens, int B, int N_kv, int chunk, int cap,
                           int HG, int nwaves) {
@@ -92,16 +93,25 @@ __device__ int unit_chunk(const int* __restrict__ kv_lens, int B, int N_kv, int 
   const int lane = (int)threadIdx.x & 63;
   float len[PER];
   float total = 0.f;
+  int lo = N_kv, hi = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int b = lane + 64 * i;
-    const int n = b < B ? (kv_lens ? kv_lens[b] : N_kv) : 0;
-    len[i] = (float)min(max(n, 0), N_kv);
+    const int n = b < B ? min(max(kv_lens ? kv_lens[b] : N_kv, 0), N_kv) : -1;
+    len[i] = (float)max(n, 0);
     total += len[i];
+    if (n >= 0) {
+      lo = min(lo, n);
+      hi = max(hi, n);
+    }
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) total += __shfl_xor(total, o);
-  if (total == 0.f) return chunk;
+  for (int o = 32; o >= 1; o >>= 1) {
+    total += __shfl_xor(total, o);
+    lo = min(lo, __shfl_xor(lo, o));
+    hi = max(hi, __shfl_xor(hi, o));
+  }
+  if (total == 0.f || lo != hi) return chunk;
   const float cf = fminf(ceilf(total * (float)HG / (float)nwaves), (float)cap);
   int c = ((int)cf + kStepKeys - 1) / kStepKeys * kStepKeys;
   c = c < chunk ? chunk : (c > cap ? cap : c);
