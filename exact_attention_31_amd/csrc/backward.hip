@@ -243,6 +243,9 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
     const int q0 = (qt0 + t % per_head) * kBwdBM;
 #pragma unroll
     for (int sub = 0; sub < kBwdBM / 32; ++sub) {
+      // one subtile at a time: interleaving the two (which the causal branch
+      // below prevents anyway) would spill
+      if constexpr (!CAUSAL) __builtin_amdgcn_sched_barrier(0);
       const int qs = q0 + 32 * sub;
       // wavefront-uniform: does any query of this subtile see any of our keys?
       if (CAUSAL && qs + 31 + off < kw) continue;
