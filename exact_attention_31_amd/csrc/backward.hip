@@ -369,7 +369,10 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   const auto rK = buffer_rsrc(K + kv_head, head_kv_bytes);
   const auto rV = buffer_rsrc(V + kv_head, head_kv_bytes);
 
-  const int q0 = wi.blk * BM + 32 * wave;
+  // causal: the block with the most keys first (blocks of a head run in order on
+  // one XCD, so the short ones come last and fill in)
+  const int qblk = CAUSAL ? nqb - 1 - wi.blk : wi.blk;
+  const int q0 = qblk * BM + 32 * wave;
   const int qrow = q0 + lr;
   const int lim = CAUSAL ? min(N_kv, max(qrow + off + 1, 0)) : N_kv;  // keys below lim visible
   u32x4_t qB[KS], gB[KS];
@@ -384,7 +387,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
 
   int kv_end = N_kv;
   if (CAUSAL) {
-    const int qlast = min(wi.blk * BM + BM - 1, N_q - 1);
+    const int qlast = min(qblk * BM + BM - 1, N_q - 1);
     kv_end = min(N_kv, max(qlast + off + 1, 0));
   }
   const int ntiles = (kv_end + kBwdBN - 1) / kBwdBN;
