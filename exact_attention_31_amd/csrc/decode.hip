@@ -111,6 +111,11 @@ __device__ int unit_chunk(const int* __restrict__ kv_lens, int B, int N_kv, int 
     lo = min(lo, __shfl_xor(lo, o));
     hi = max(hi, __shfl_xor(hi, o));
   }
+  // every lane holds the reductions; taking lane 0's keeps the decisions (and
+  // the result) in scalar registers
+  total = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, total)));
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  hi = __builtin_amdgcn_readfirstlane(hi);
   if (total == 0.f || lo != hi) return chunk;
   const float cf = fminf(ceilf(total * (float)HG / (float)nwaves), (float)cap);
   int c = ((int)cf + kStepKeys - 1) / kStepKeys * kStepKeys;
@@ -122,11 +127,12 @@ __device__ int unit_chunk(const int* __restrict__ kv_lens, int B, int N_kv, int 
     for (int i = 0; i < PER; ++i) units += ceilf(len[i] * rc);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) units += __shfl_xor(units, o);
+    units = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, units)));
     if (units * (float)HG <= (float)nwaves) break;
     const int step = (c / 16 + kStepKeys - 1) / kStepKeys * kStepKeys;
     c = c + step > cap ? cap : c + step;
   }
-  return __builtin_amdgcn_readfirstlane(c);
+  return c;
 }
 
 // Four FP8 E4M3 codes (one dword) to four bf16 values (two dwords), exactly:
