@@ -57,6 +57,7 @@ template <int D> struct Lds16 {
 // rescale of l and u. Probabilities then stay below 2^8, and l and u keep one
 // common reference point, so u / l is unchanged.
 constexpr float kLazyRescale = 8.f;
+constexpr float kLazySum = 256.f;  // 2^kLazyRescale
 
 // QB query blocks of 32 rows per wavefront (NW * 32 * QB rows per
 // workgroup). Each K or V operand read from LDS feeds QB MFMAs, so QB = 2
@@ -704,33 +705,67 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<1, D>::kWaves)) void pr
             s1[r] = (e + 32 < rel) ? s1[r] : kNegInf;
           }
         }
-        // ---- row max of the raw scores (scale > 0 commutes with max)
-        float mx = max3(s0[0], s0[1], s1[0]);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = max3(mx, s0[r], s1[r]);
-        mx = fmaxf(mx, s1[0]);
-        const float mxs = half_max(mx) * scale_log2;
-        // wavefront-uniform branch; each lane moves only its own reference
-        const bool need = mxs > m + kLazyRescale;
-        if (wave_any(need)) {
-          const float alpha = need ? ((m == kNegInf) ? 0.f : fast_exp2(m - mxs)) : 1.f;
-          m = need ? mxs : m;
-          l *= alpha;
-#pragma unroll
-          for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-        }
-        const float nm = (m == kNegInf) ? 0.f : -m;
-        // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
         uint32_t pk[16];
+        // ---- fast path (d = 64, where the vector ALUs bound the loop): the
+        // exponentials against the current reference m, without the tile's row
+        // maximum. If this lane's 32 of them sum to at most 2^kLazyRescale, each
+        // is at most that, which is all the lazy rescale rule asks. Otherwise
+        // (or while m is still -inf) the full rule below runs on the same
+        // scores, raising m to the tile's maximum.
+        bool slow = true;
+        bool raise_all = false;
+        if constexpr (D == 64) {
+          slow = wave_any(m == kNegInf);
+          if (!slow) {
+            const float nmf = -m;
+            float ts = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(s0[r], scale_log2, nm));
-          const float p1 = fast_exp2(__builtin_fmaf(s0[r + 1], scale_log2, nm));
-          const float p2 = fast_exp2(__builtin_fmaf(s1[r], scale_log2, nm));
-          const float p3 = fast_exp2(__builtin_fmaf(s1[r + 1], scale_log2, nm));
-          l += (p0 + p1) + (p2 + p3);
-          pk[r >> 1] = TT::pack2(p0, p1);
-          pk[8 + (r >> 1)] = TT::pack2(p2, p3);
+            for (int r = 0; r < 16; r += 2) {
+              const float p0 = fast_exp2(__builtin_fmaf(s0[r], scale_log2, nmf));
+              const float p1 = fast_exp2(__builtin_fmaf(s0[r + 1], scale_log2, nmf));
+              const float p2 = fast_exp2(__builtin_fmaf(s1[r], scale_log2, nmf));
+              const float p3 = fast_exp2(__builtin_fmaf(s1[r + 1], scale_log2, nmf));
+              ts += (p0 + p1) + (p2 + p3);
+              pk[r >> 1] = TT::pack2(p0, p1);
+              pk[8 + (r >> 1)] = TT::pack2(p2, p3);
+            }
+            if (wave_any(!(ts <= kLazySum))) {  // (also catches inf and NaN)
+              slow = true;
+              raise_all = true;
+            } else {
+              l += ts;
+            }
+          }
+        }
+        if (slow) {
+          // ---- row max of the raw scores (scale > 0 commutes with max)
+          float mx = max3(s0[0], s0[1], s1[0]);
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = max3(mx, s0[r], s1[r]);
+          mx = fmaxf(mx, s1[0]);
+          const float mxs = half_max(mx) * scale_log2;
+          // wavefront-uniform branch; each lane moves only its own reference
+          // (after a failed fast path, to the tile's maximum whenever it is higher)
+          const bool need = raise_all ? (mxs > m) : (mxs > m + kLazyRescale);
+          if (wave_any(need)) {
+            const float alpha = need ? ((m == kNegInf) ? 0.f : fast_exp2(m - mxs)) : 1.f;
+            m = need ? mxs : m;
+            l *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+          }
+          const float nm = (m == kNegInf) ? 0.f : -m;
+          // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(__builtin_fmaf(s0[r], scale_log2, nm));
+            const float p1 = fast_exp2(__builtin_fmaf(s0[r + 1], scale_log2, nm));
+            const float p2 = fast_exp2(__builtin_fmaf(s1[r], scale_log2, nm));
+            const float p3 = fast_exp2(__builtin_fmaf(s1[r + 1], scale_log2, nm));
+            l += (p0 + p1) + (p2 + p3);
+            pk[r >> 1] = TT::pack2(p0, p1);
+            pk[8 + (r >> 1)] = TT::pack2(p2, p3);
+          }
         }
         // ---- O^T += V^T P^T, four 16-key steps
 #pragma unroll

@@ -186,3 +186,31 @@ def test_prefill_variants_match_oracle(variant, monkeypatch):
             ((1, 4, 2, 300, 300, 128), True, "bf16"), ((2, 2, 2, 129, 257, 64), True, "f16"),
             ((1, 8, 8, 200, 200, 128), False, "f16"), ((1, 2, 1, 70, 30, 64), True, "bf16")]):
         _run_small(*shape, dtype, causal, seed=100 + 10 * int(variant) + i)
+
+
+@pytest.mark.parametrize("rising", [True, False], ids=["rising", "falling"])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("d,dtype", [(64, "f16"), (64, "bf16"), (128, "bf16")])
+def test_prefill_rescales_when_scores_grow_along_the_keys(d, dtype, causal, rising):
+    """Key norms grow by 1.5x per 64 keys (or shrink): with rising scores every
+    tile's maximum exceeds the row's reference by more than the lazy-rescale
+    margin, so the rescale path runs on most tiles (at d = 64 also the fallback
+    from the max-free fast path); with falling scores it almost never does."""
+    B, H, N = 1, 4, 700
+    seed = zlib.crc32(repr((d, dtype, causal, rising)).encode()) % 10000
+    _announce(f"prefill growing scores d={d} {dtype} causal={causal} rising={rising}")
+    q = A.random_tensor((B, H, N, d), seed * 3, dtype)
+    k = A.random_tensor((B, H, N, d), seed * 3 + 1, dtype)
+    v = A.random_tensor((B, H, N, d), seed * 3 + 2, dtype)
+    f = 1.5 ** (np.arange(N) / 64.0)
+    if not rising:
+        f = f[::-1]
+    k = A.round_to_dtype((k * f[None, None, :, None].astype(np.float32)).astype(np.float32), dtype)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = E.attn_prefill_fwd(to_device(q, dtype), to_device(k, dtype), to_device(v, dtype),
+                                causal=causal, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    oref, lref = attention_ref(q, k, v, causal, scale)
+    err = max_abs_err(to_host64(o), oref)
+    assert err <= TOL_O[dtype], f"max |err| {err}"
+    check_lse(lse.cpu().numpy().astype(np.float64), lref, TOL_LSE[dtype])
