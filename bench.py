@@ -229,10 +229,16 @@ def bench_decode_fp8(cfg, steps, warmup, torch, E, cache, k_scale=2.0 ** -6, v_s
     ms, wall = time_launches(call, steps, warmup, torch)
     nbytes = decode_kv_bytes(cfg, lens) // 2
     gbs = nbytes / (ms * 1e-3) / 1e9
-    del kc, vc, q, o, ws
+    # what the quantisation costs: the same step over the unquantised bf16 cache
+    o16 = E.attn_decode_fwd(q, k, v, kv_lens=lens_d, scale=cfg.scale, causal=cfg.causal)
+    diff = (o.float() - o16.float()).abs()
+    err = {"max_abs_diff_vs_bf16_cache": float(diff.max()),
+           "mean_abs_diff_vs_bf16_cache": float(diff.mean()),
+           "mean_abs_output": float(o16.float().abs().mean())}
+    del kc, vc, q, o, ws, o16, diff
     return {"config": f"{cfg.cid}-fp8", "name": cfg.name + ", FP8 E4M3 cache", "ms": ms,
             "kv_bytes": nbytes, "gb_per_s": gbs, "frac_of_peak": gbs / PEAK_HBM,
-            "peak_gb_per_s": PEAK_HBM, "wall_s": wall}
+            "peak_gb_per_s": PEAK_HBM, "wall_s": wall, **err}
 
 
 def bench_backward(cfg, steps, warmup, torch, E):
@@ -390,6 +396,8 @@ def main(argv=None):
         res["decode_multi"] = r
         if args.only == "decode_multi":
             res["decode"] = r
+            res["decode_label"] = ("GQA multi-token decode, bf16, B=64, 4 new tokens per request "
+                                   "(causal), H_q=32, H_kv=4, d=128, KV 32768")
         r, cache = bench_decode(A.CONFIGS[8], args.steps, args.warmup, torch, E, cache=cache)
         print(f"# decode c5, 64 tokens: {r['ms']:.3f} ms  {r['gb_per_s']:.0f} GB/s  "
               f"{r['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
@@ -403,6 +411,8 @@ def main(argv=None):
         res["decode_paged"] = r
         if args.only == "decode_paged":
             res["decode"] = r
+            res["decode_label"] = ("GQA decode over a paged cache (block 16), bf16, B=64, H_q=32, "
+                                   "H_kv=4, d=128, KV 32768")
     if args.only in (None, "decode_fp8"):
         if cache is None:
             _, cache = bench_decode(A.CONFIGS[5], 1, 1, torch, E)
@@ -412,11 +422,15 @@ def main(argv=None):
         res["decode_fp8"] = r
         if args.only == "decode_fp8":
             res["decode"] = r
+            res["decode_label"] = ("GQA decode over an FP8 E4M3 cache, bf16 queries, B=64, H_q=32, "
+                                   "H_kv=4, d=128, KV 32768")
     extra = []
     if args.only == "decode_ragged":
         r, cache = bench_decode(A.CONFIGS[6], args.steps, args.warmup, torch, E, ragged=True)
         print(f"# decode c5 ragged: {r['ms']:.3f} ms  {r['gb_per_s']:.0f} GB/s", file=sys.stderr, flush=True)
         res["decode"] = r
+        res["decode_label"] = ("GQA decode, bf16, B=64, H_q=32, H_kv=4, d=128, KV lengths "
+                               "uniform on 1..32768")
     if args.all:
         for cid in (1, 3, 4):
             r = bench_prefill(A.CONFIGS[cid], max(5, args.steps // 5) if cid == 4 else args.steps,
@@ -446,7 +460,8 @@ def main(argv=None):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "causal MHA prefill, bf16, B=4, H_q=H_kv=32, N=4096, d=128"
-                   if p else "GQA decode, bf16, B=64, H_q=32, H_kv=4, d=128, KV 32768",
+                   if p else res.get("decode_label",
+                                     "GQA decode, bf16, B=64, H_q=32, H_kv=4, d=128, KV 32768"),
                    "B": 4 if p else 64, "seq_len": 4096 if p else 32768, "head_dim": 128,
                    "causal": bool(p), "parallelism": "single GPU"},
     }
@@ -460,13 +475,15 @@ def main(argv=None):
             line["roofline"]["library_gemm_tflops"] = round(res["gemm"], 1)
             line["roofline"]["frac_of_library_gemm"] = round(p["tflops"] / res["gemm"], 4)
     if d:
-        line["decode"] = {"workload": "GQA decode, bf16, B=64, H_q=32, H_kv=4 (G=8), d=128, "
-                                      "KV 32768 per request", "ms_per_step": round(d["ms"], 5),
+        line["decode"] = {"workload": res.get("decode_label", "GQA decode, bf16, B=64, H_q=32, H_kv=4 "
+                                                              "(G=8), d=128, KV 32768 per request"),
+                          "ms_per_step": round(d["ms"], 5),
                           "value": round(d["gb_per_s"], 2), "unit": "GB/s",
                           "frac_of_hbm_peak": round(d["frac_of_peak"], 4)}
         line["decode_roofline"] = {"bound": "hbm", "achieved": round(d["gb_per_s"], 2), "peak": PEAK_HBM,
                                    "unit": "GB/s", "frac": round(d["frac_of_peak"], 4),
-                                   "traffic": measured_traffic("decode"),
+                                   # counters were taken on the plain decode workload only
+                                   "traffic": None if "decode_label" in res else measured_traffic("decode"),
                                    "kernel": "decode_split_kernel + decode_merge_kernel (one step)",
                                    "work_per_launch": d["kv_bytes"]}
     dm = res.get("decode_multi")
@@ -502,6 +519,9 @@ def main(argv=None):
                         "output, B=64, H_q=32, H_kv=4, d=128, KV 32768 per request",
             "ms_per_step": round(df8["ms"], 5), "value": round(df8["gb_per_s"], 2), "unit": "GB/s",
             "frac_of_hbm_peak": round(df8["frac_of_peak"], 4),
+            "max_abs_diff_vs_bf16_cache": round(df8["max_abs_diff_vs_bf16_cache"], 6),
+            "mean_abs_diff_vs_bf16_cache": round(df8["mean_abs_diff_vs_bf16_cache"], 6),
+            "mean_abs_output": round(df8["mean_abs_output"], 6),
             "kernel": "decode_split_kernel<fp8> + decode_merge_kernel (one step)"}
     bw = res.get("backward")
     if bw:
