@@ -341,6 +341,39 @@ def cpu_baseline(cfg, budget_s=15.0):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def cpu_baseline_decode(cfg, budget_s=5.0):
+    """The float64 oracle on a bounded sample of the decode workload: whole
+    requests (all KV heads, each with its G query heads), KV bytes per second
+    counted as the GPU's (the cache's 16-bit bytes)."""
+    import attn_inputs as A
+    from oracle import attention_head_rows
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        threads = 1
+    done, elapsed = 0, 0.0
+    t_start = time.perf_counter()
+    while elapsed < budget_s and done < cfg.B:
+        b = done
+        for g in range(cfg.H_kv):
+            k = A.slice_values(cfg.cid, "k", b, g, cfg.N_kv, cfg.d, cfg.sigma, cfg.dtype)
+            v = A.slice_values(cfg.cid, "v", b, g, cfg.N_kv, cfg.d, cfg.sigma, cfg.dtype)
+            qs = [A.slice_values(cfg.cid, "q", b, g * cfg.G + j, cfg.N_q, cfg.d, cfg.sigma, cfg.dtype)
+                  for j in range(cfg.G)]
+            t0 = time.perf_counter()
+            for q in qs:
+                attention_head_rows(q, np.arange(cfg.N_q), cfg.N_q, k, v, cfg.causal, cfg.scale)
+            elapsed += time.perf_counter() - t0
+        done += 1
+        if time.perf_counter() - t_start > 6 * budget_s:
+            break
+    nbytes = done * cfg.H_kv * cfg.N_kv * cfg.d * 2 * 2
+    return {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {cfg.B} requests (all {cfg.H_kv} KV heads x {cfg.G} query heads, "
+                      f"{cfg.N_kv} keys each, float64 numpy, {elapsed:.1f} s)"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -445,6 +478,9 @@ def main(argv=None):
     cpu = None
     if not args.no_cpu and "prefill" in res:
         cpu = cpu_baseline(A.CONFIGS[2], args.cpu_budget)
+    cpu_dec = None
+    if not args.no_cpu and "decode" in res and "decode_label" not in res:
+        cpu_dec = cpu_baseline_decode(A.CONFIGS[5], max(2.0, args.cpu_budget / 3))
 
     p = res.get("prefill")
     d = res.get("decode")
@@ -480,6 +516,8 @@ def main(argv=None):
                           "ms_per_step": round(d["ms"], 5),
                           "value": round(d["gb_per_s"], 2), "unit": "GB/s",
                           "frac_of_hbm_peak": round(d["frac_of_peak"], 4)}
+        if cpu_dec is not None:
+            line["decode"]["cpu_baseline"] = cpu_dec
         line["decode_roofline"] = {"bound": "hbm", "achieved": round(d["gb_per_s"], 2), "peak": PEAK_HBM,
                                    "unit": "GB/s", "frac": round(d["frac_of_peak"], 4),
                                    # counters were taken on the plain decode workload only
