@@ -35,7 +35,24 @@ constexpr int kBwdNWK = 8;   // wavefronts per dK/dV workgroup (two per SIMD)
 constexpr int kBwdKW = 32 * kBwdNWK;  // keys per dK/dV workgroup
 
 template <int D> struct BwdLds {
-  static constexpr int STR = D + 8;  // row stride (elements) of staged Q, dO, K, V rows
+  // row stride (elements) of LDS tiles read only row-wise (16-byte reads): rows
+  // 4 (mod 64) dwords apart, so 16 consecutive rows cover the 64 banks once
+  static constexpr int STR = D + 8;
+};
+
+// Placement of LDS tiles read both row-wise (16-byte reads, 16 lanes per LDS
+// cycle) and by transposing 8-byte reads (32 lanes: 4 consecutive rows x 16
+// dwords). Rows go in groups of four: IN elements apart within a group (16
+// mod 64 dwords, so the 4 rows of a transposing read use disjoint banks) and
+// GRP elements apart between groups (4 * odd mod 64 dwords, which with the
+// in-group step puts 16 consecutive rows on 16 distinct 4-bank sets). A plain
+// stride cannot do both: the two reads need it 16 and 4 * odd (mod 64) dwords.
+template <int D> struct BwdGrp {
+  static constexpr int IN = (D == 128) ? 160 : 96;
+  static constexpr int GRP = (D == 128) ? 616 : 360;
+  static_assert(GRP >= 3 * IN + D, "rows of a group must not overlap");
+  static constexpr int size(int rows) { return GRP * (rows / 4); }
+  static __device__ __forceinline__ int row(int r) { return GRP * (r >> 2) + IN * (r & 3); }
 };
 
 // Workgroup -> (batch, head, block) with the same XCD-contiguous order as the
@@ -130,8 +147,9 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
   constexpr int NT = 64 * kBwdNWK;
   constexpr int LPT = kBwdBM * CPR / NT;  // 16-byte loads per thread per tile, per tensor
   static_assert(LPT * NT == kBwdBM * CPR, "tile load must split evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kBwdBM * STR];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[2][kBwdBM * STR];
+  using Gp = BwdGrp<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][Gp::size(kBwdBM)];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[2][Gp::size(kBwdBM)];
   __shared__ __attribute__((aligned(16))) float sL[2][kBwdBM];
   __shared__ __attribute__((aligned(16))) float sD[2][kBwdBM];
   __shared__ __attribute__((aligned(16))) uint16_t sVk[kBwdKW * STR];  // this workgroup's V rows
@@ -186,7 +204,7 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
   for (int i = 0; i < LPT; ++i) {
     const int c = tid + NT * i;
     ld_off[i] = (uint32_t)((c / CPR) * D + (c % CPR) * 8) * 2;
-    st_off[i] = (c / CPR) * STR + (c % CPR) * 8;
+    st_off[i] = Gp::row(c / CPR) + (c % CPR) * 8;
   }
   u32x4_t qbuf[LPT], gbuf[LPT];
   float lbuf = 0.f;
@@ -226,8 +244,8 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
   // per-lane LDS offsets: A rows (lane's row lr, columns 16*st + 8*lh) and the
   // transposing read (lane i of 16-lane group g: row 4*(g/2) + i/4, columns
   // 16*(g%2) + 4*(i%4) of a 4 x 32 block)
-  const int a_lane = lr * STR + 8 * lh;
-  const int t_lane = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * STR + 16 * ((lane >> 4) & 1) +
+  const int a_lane = Gp::row(lr) + 8 * lh;
+  const int t_lane = Gp::row(4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) + 16 * ((lane >> 4) & 1) +
                      4 * (lane & 3);
 
   if (ntiles > 0) {
@@ -249,8 +267,8 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
       const int qs = q0 + 32 * sub;
       // wavefront-uniform: does any query of this subtile see any of our keys?
       if (CAUSAL && qs + 31 + off < kw) continue;
-      const uint16_t* tq = &sQ[buf][0] + 32 * sub * STR;
-      const uint16_t* tg = &sG[buf][0] + 32 * sub * STR;
+      const uint16_t* tq = &sQ[buf][0] + 8 * Gp::GRP * sub;  // row 32*sub
+      const uint16_t* tg = &sG[buf][0] + 8 * Gp::GRP * sub;
       f32x16_t s = f32x16_t{0}, dp = f32x16_t{0};
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
@@ -290,10 +308,11 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
         const u32x4_t bd = {pd[4 * j], pd[4 * j + 1], pd[4 * j + 2], pd[4 * j + 3]};
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* pg = tg + 16 * j * STR + t_lane + 32 * db;
-          const uint16_t* pq = tq + 16 * j * STR + t_lane + 32 * db;
-          const u32x2_t g_lo = lds_read_tr16(pg), g_hi = lds_read_tr16(pg + 8 * STR);
-          const u32x2_t q_lo = lds_read_tr16(pq), q_hi = lds_read_tr16(pq + 8 * STR);
+          // rows 16*j + (0..7), then + 8
+          const uint16_t* pg = tg + 4 * Gp::GRP * j + t_lane + 32 * db;
+          const uint16_t* pq = tq + 4 * Gp::GRP * j + t_lane + 32 * db;
+          const u32x2_t g_lo = lds_read_tr16(pg), g_hi = lds_read_tr16(pg + 2 * Gp::GRP);
+          const u32x2_t q_lo = lds_read_tr16(pq), q_hi = lds_read_tr16(pq + 2 * Gp::GRP);
           dvT[db] = TT::mfma32(u32x4_t{g_lo[0], g_lo[1], g_hi[0], g_hi[1]}, bp, dvT[db]);
           dkT[db] = TT::mfma32(u32x4_t{q_lo[0], q_lo[1], q_hi[0], q_hi[1]}, bd, dkT[db]);
         }
@@ -346,7 +365,9 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   constexpr int LPT = kBwdBN * CPR / NT;
   constexpr int BM = 32 * NW;
   static_assert(LPT * NT == kBwdBN * CPR, "tile load must split evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBwdBN * STR];
+  using Gp = BwdGrp<D>;
+  // K is read row-wise and transposed (grouped rows), V only row-wise
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][Gp::size(kBwdBN)];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBwdBN * STR];
 
   const int tid = threadIdx.x;
@@ -393,12 +414,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   const int ntiles = (kv_end + kBwdBN - 1) / kBwdBN;
 
   uint32_t ld_off[LPT];
-  int st_off[LPT];
+  int st_k[LPT], st_v[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int c = tid + NT * i;
     ld_off[i] = (uint32_t)((c / CPR) * D + (c % CPR) * 8) * 2;
-    st_off[i] = (c / CPR) * STR + (c % CPR) * 8;
+    st_k[i] = Gp::row(c / CPR) + (c % CPR) * 8;
+    st_v[i] = (c / CPR) * STR + (c % CPR) * 8;
   }
   u32x4_t kbuf[LPT], vbuf[LPT];
   auto load_tile = [&](int t) {
@@ -412,16 +434,17 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      *(u32x4_t*)(&sK[buf][st_off[i]]) = kbuf[i];
-      *(u32x4_t*)(&sV[buf][st_off[i]]) = vbuf[i];
+      *(u32x4_t*)(&sK[buf][st_k[i]]) = kbuf[i];
+      *(u32x4_t*)(&sV[buf][st_v[i]]) = vbuf[i];
     }
   };
 
   f32x16_t dqT[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) dqT[i] = f32x16_t{0};
-  const int a_lane = lr * STR + 8 * lh;
-  const int t_lane = (4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * STR + 16 * ((lane >> 4) & 1) +
+  const int ak_lane = Gp::row(lr) + 8 * lh;
+  const int av_lane = lr * STR + 8 * lh;
+  const int t_lane = Gp::row(4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) + 16 * ((lane >> 4) & 1) +
                      4 * (lane & 3);
 
   if (ntiles > 0) {
@@ -440,13 +463,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
       const int ks = kv0 + 32 * kb;
       // wavefront-uniform: does any of our rows see any key of this half?
       if (CAUSAL && ks > q0 + 31 + off) continue;
-      const uint16_t* tk = &sK[buf][0] + 32 * kb * STR;
+      const uint16_t* tk = &sK[buf][0] + 8 * Gp::GRP * kb;  // row 32*kb
       const uint16_t* tv = &sV[buf][0] + 32 * kb * STR;
       f32x16_t s = f32x16_t{0}, dp = f32x16_t{0};
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        const u32x4_t ak = *(const u32x4_t*)(tk + a_lane + 16 * st);
-        const u32x4_t av = *(const u32x4_t*)(tv + a_lane + 16 * st);
+        const u32x4_t ak = *(const u32x4_t*)(tk + ak_lane + 16 * st);
+        const u32x4_t av = *(const u32x4_t*)(tv + av_lane + 16 * st);
         s = TT::mfma32(ak, qB[st], s);
         dp = TT::mfma32(av, gB[st], dp);
       }
@@ -469,8 +492,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
         const u32x4_t bd = {pd[4 * j], pd[4 * j + 1], pd[4 * j + 2], pd[4 * j + 3]};
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* pk = tk + 16 * j * STR + t_lane + 32 * db;
-          const u32x2_t lo = lds_read_tr16(pk), hi = lds_read_tr16(pk + 8 * STR);
+          const uint16_t* pk = tk + 4 * Gp::GRP * j + t_lane + 32 * db;  // rows 16*j + ...
+          const u32x2_t lo = lds_read_tr16(pk), hi = lds_read_tr16(pk + 2 * Gp::GRP);
           dqT[db] = TT::mfma32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, bd, dqT[db]);
         }
       }
