@@ -42,11 +42,12 @@ template <int D> struct BwdLds {
 
 // Placement of LDS tiles read both row-wise (16-byte reads, 16 lanes per LDS
 // cycle) and by transposing 8-byte reads (32 lanes: 4 consecutive rows x 16
-// dwords). Rows go in groups of four: IN elements apart within a group (16
-// mod 64 dwords, so the 4 rows of a transposing read use disjoint banks) and
-// GRP elements apart between groups (4 * odd mod 64 dwords, which with the
-// in-group step puts 16 consecutive rows on 16 distinct 4-bank sets). A plain
-// stride cannot do both: the two reads need it 16 and 4 * odd (mod 64) dwords.
+// dwords). Rows go in groups of four: IN elements apart within a group (an odd
+// multiple of 16 dwords mod 64, so the 4 rows of a transposing read use
+// disjoint banks) and GRP elements apart between groups (an odd multiple of 4
+// dwords mod 64, which with the in-group step puts 16 consecutive rows on 16
+// distinct 4-bank sets). A plain stride cannot do both: the two reads need it
+// 16 * odd and 4 * odd (mod 64) dwords.
 template <int D> struct BwdGrp {
   static constexpr int IN = (D == 128) ? 160 : 96;
   static constexpr int GRP = (D == 128) ? 616 : 360;
