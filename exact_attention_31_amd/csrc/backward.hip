@@ -260,10 +260,11 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
     const int buf = t & 1;
     if (t + 1 < ntiles) load_tile(t + 1);
     const int q0 = (qt0 + t % per_head) * kBwdBM;
-#pragma unroll
+    // one subtile at a time, as a rolled loop: interleaving the two would
+    // spill, and unrolled, the subtile skip and the two forms of P keep more
+    // registers live (measured slower)
+#pragma unroll 1
     for (int sub = 0; sub < kBwdBM / 32; ++sub) {
-      // one subtile at a time: interleaving the two (which the causal branch
-      // below prevents anyway) would spill
       if constexpr (!CAUSAL) __builtin_amdgcn_sched_barrier(0);
       const int qs = q0 + 32 * sub;
       // wavefront-uniform: does any query of this subtile see any of our keys?
@@ -282,24 +283,32 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
       const bool need_mask = CAUSAL && (kw + 31 > qs + off);
       const int key = kw + lr;
       uint32_t pp[8], pd[8];
+      // (one branch for the subtile: the masked and unmasked forms are
+      // separate straight-line code)
+      auto form_p = [&](bool masked) {
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const f32x4_t L4 = *(const f32x4_t*)(&sL[buf][32 * sub + 8 * rg + 4 * lh]);
-        const f32x4_t D4 = *(const f32x4_t*)(&sD[buf][32 * sub + 8 * rg + 4 * lh]);
-        float p[4], ds[4];
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4_t L4 = *(const f32x4_t*)(&sL[buf][32 * sub + 8 * rg + 4 * lh]);
+          const f32x4_t D4 = *(const f32x4_t*)(&sD[buf][32 * sub + 8 * rg + 4 * lh]);
+          float p[4], ds[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * rg + i;
-          float pv = fast_exp2(__builtin_fmaf(s[r], scale_log2, -L4[i]));
-          if (need_mask) pv = (key <= qs + 8 * rg + 4 * lh + i + off) ? pv : 0.f;
-          p[i] = pv;
-          ds[i] = pv * (dp[r] - D4[i]);
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * rg + i;
+            float pv = fast_exp2(__builtin_fmaf(s[r], scale_log2, -L4[i]));
+            if (masked) pv = (key <= qs + 8 * rg + 4 * lh + i + off) ? pv : 0.f;
+            p[i] = pv;
+            ds[i] = pv * (dp[r] - D4[i]);
+          }
+          pp[2 * rg] = TT::pack2(p[0], p[1]);
+          pp[2 * rg + 1] = TT::pack2(p[2], p[3]);
+          pd[2 * rg] = TT::pack2(ds[0], ds[1]);
+          pd[2 * rg + 1] = TT::pack2(ds[2], ds[3]);
         }
-        pp[2 * rg] = TT::pack2(p[0], p[1]);
-        pp[2 * rg + 1] = TT::pack2(p[2], p[3]);
-        pd[2 * rg] = TT::pack2(ds[0], ds[1]);
-        pd[2 * rg + 1] = TT::pack2(ds[2], ds[3]);
-      }
+      };
+      if (need_mask)
+        form_p(true);
+      else
+        form_p(false);
       // dV^T += dO^T P and dK^T += Q^T dS over this subtile's 32 queries (two k-steps
       // of 16: accumulator rows 0..7 then 8..15, i.e. queries 4*lh + {0..3, 8..11}
       // and 16 + the same)
@@ -459,7 +468,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
     const int buf = t & 1;
     if (t + 1 < ntiles) load_tile(t + 1);
     const int kv0 = t * kBwdBN;
-#pragma unroll
+#pragma unroll 1
     for (int kb = 0; kb < kBwdBN / 32; ++kb) {
       const int ks = kv0 + 32 * kb;
       // wavefront-uniform: does any of our rows see any key of this half?
@@ -477,17 +486,25 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
       // rows of accumulator r: key ks + 8*(r/4) + 4*lh + r%4; column: this lane's row
       const bool need_mask = ks + 32 > N_kv || (CAUSAL && ks + 31 > q0 + off);
       uint32_t pd[8];
+      // (one branch for the half: the masked and unmasked forms are separate
+      // straight-line code)
+      auto form_ds = [&](bool masked) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float p0 = fast_exp2(__builtin_fmaf(s[r], scale_log2, -L2));
-        float p1 = fast_exp2(__builtin_fmaf(s[r + 1], scale_log2, -L2));
-        if (need_mask) {
-          const int key = ks + 8 * (r >> 2) + 4 * lh + (r & 3);
-          p0 = key < lim ? p0 : 0.f;
-          p1 = key + 1 < lim ? p1 : 0.f;
+        for (int r = 0; r < 16; r += 2) {
+          float p0 = fast_exp2(__builtin_fmaf(s[r], scale_log2, -L2));
+          float p1 = fast_exp2(__builtin_fmaf(s[r + 1], scale_log2, -L2));
+          if (masked) {
+            const int key = ks + 8 * (r >> 2) + 4 * lh + (r & 3);
+            p0 = key < lim ? p0 : 0.f;
+            p1 = key + 1 < lim ? p1 : 0.f;
+          }
+          pd[r >> 1] = TT::pack2(p0 * (dp[r] - Dl), p1 * (dp[r + 1] - Dl));
         }
-        pd[r >> 1] = TT::pack2(p0 * (dp[r] - Dl), p1 * (dp[r + 1] - Dl));
-      }
+      };
+      if (need_mask)
+        form_ds(true);
+      else
+        form_ds(false);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const u32x4_t bd = {pd[4 * j], pd[4 * j + 1], pd[4 * j + 2], pd[4 * j + 3]};
