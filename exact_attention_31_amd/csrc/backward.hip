@@ -281,7 +281,9 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
       }
       // rows of accumulator r: query qs + 8*(r/4) + 4*lh + r%4; column: key kw + lr
       const bool need_mask = CAUSAL && (kw + 31 > qs + off);
-      const int key = kw + lr;
+      // element (rg, i) is query qs + 8*rg + 4*lh + i; key kw + lr is visible
+      // to it iff 8*rg + i >= thr
+      const int thr = kw + lr - qs - off - 4 * lh;
       uint32_t pp[8], pd[8];
       // (one branch for the subtile: the masked and unmasked forms are
       // separate straight-line code)
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * rg + i;
             float pv = fast_exp2(__builtin_fmaf(s[r], scale_log2, -L4[i]));
-            if (masked) pv = (key <= qs + 8 * rg + 4 * lh + i + off) ? pv : 0.f;
+            if (masked) pv = (8 * rg + i >= thr) ? pv : 0.f;
             p[i] = pv;
             ds[i] = pv * (dp[r] - D4[i]);
           }
@@ -488,15 +490,17 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
       uint32_t pd[8];
       // (one branch for the half: the masked and unmasked forms are separate
       // straight-line code)
+      // register r holds key ks + 4*lh + e, e = 8*(r/4) + r%4: visible iff e < thr
+      const int thr = lim - ks - 4 * lh;
       auto form_ds = [&](bool masked) {
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           float p0 = fast_exp2(__builtin_fmaf(s[r], scale_log2, -L2));
           float p1 = fast_exp2(__builtin_fmaf(s[r + 1], scale_log2, -L2));
           if (masked) {
-            const int key = ks + 8 * (r >> 2) + 4 * lh + (r & 3);
-            p0 = key < lim ? p0 : 0.f;
-            p1 = key + 1 < lim ? p1 : 0.f;
+            const int e = 8 * (r >> 2) + (r & 3);
+            p0 = e < thr ? p0 : 0.f;
+            p1 = e + 1 < thr ? p1 : 0.f;
           }
           pd[r >> 1] = TT::pack2(p0 * (dp[r] - Dl), p1 * (dp[r + 1] - Dl));
         }
