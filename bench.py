@@ -261,10 +261,13 @@ def bench_backward(cfg, steps, warmup, torch, E):
     ms, wall = time_launches(call, steps, warmup, torch)
     flops = prefill_flops(cfg) * 10 // 4
     tflops = flops / (ms * 1e-3) / 1e12
+    # Q, K, V, O, dO read and dQ, dK, dV written once each, plus the LSE
+    nbytes = sum(t.numel() * t.element_size() for t in (q, k, v, o, do, dq, dk, dv))
+    nbytes += lse.numel() * lse.element_size()
     del q, k, v, o, do, dq, dk, dv, ws
     return {"config": f"{cfg.cid}-bwd", "name": cfg.name + ", backward", "ms": ms, "flops": flops,
             "tflops": tflops, "frac_of_peak": tflops / PEAK_MFMA_16BIT, "peak_tflops": PEAK_MFMA_16BIT,
-            "wall_s": wall}
+            "bytes": nbytes, "wall_s": wall}
 
 
 def library_gemm_tflops(torch, n=8192, steps=20):
@@ -568,6 +571,9 @@ def main(argv=None):
                         "(given the forward's O and LSE)",
             "ms_per_step": round(bw["ms"], 5), "value": round(bw["tflops"], 2), "unit": "TFLOP/s",
             "frac_of_mfma_peak": round(bw["frac_of_peak"], 4), "work_per_launch": bw["flops"],
+            # Q, K, V, O, dO and the LSE read once, dQ, dK, dV written once
+            "algorithmic_bytes": bw["bytes"],
+            "traffic": measured_traffic("backward"),
             "kernel": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel (one step)"}
     if p:
         line["prefill_first_call_ms"] = round(p["first_call_ms"], 3)
