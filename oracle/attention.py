@@ -86,6 +86,23 @@ def visible_pairs(N_q: int, n: int, causal: bool) -> int:
     return total
 
 
+def softmax_stats(scores: np.ndarray):
+    """The two-pass softmax of each score row (last axis), float64.
+
+    Pass one takes the row maximum m over the finite entries; pass two forms
+    p = exp(s - m) and their sum l. Subtracting m changes only the
+    representation of the probabilities p / l, not their values (auturnal.com
+    guide, section 8), and keeps exp from overflowing for large scores.
+    Entries of -inf (masked keys) get p = 0. A row with no finite entry has
+    m = 0 and l = 0. Returns (p, m, l).
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    m = s.max(axis=-1)
+    m = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(s - m[..., None])
+    return p, m, p.sum(axis=-1)
+
+
 def _head(q_rows: np.ndarray, rows: np.ndarray, N_q: int, k: np.ndarray, v: np.ndarray,
           causal: bool, scale: float, n: int, row_block: int = 512):
     """One head. q_rows [len(rows), d] are the queries at sequence positions `rows`
@@ -110,15 +127,12 @@ def _head(q_rows: np.ndarray, rows: np.ndarray, N_q: int, k: np.ndarray, v: np.n
             masked = keys[None, :] > (r[:, None] + off)
             scores = np.where(masked, -np.inf, scores)
         # 3. two-pass softmax over the key axis
-        m = scores.max(axis=1)
-        empty = ~np.isfinite(m)            # no visible key
-        m_safe = np.where(empty, 0.0, m)
-        p = np.exp(scores - m_safe[:, None])
-        l = p.sum(axis=1)
+        p, m, l = softmax_stats(scores)
+        empty = l == 0.0                   # no visible key
         # 4. weighted sum of V, normalised
         with np.errstate(invalid="ignore", divide="ignore"):
             out = (p @ vv) / l[:, None]
-            row_lse = m_safe + np.log(l)
+            row_lse = m + np.log(l)
         out[empty] = 0.0
         row_lse[empty] = -np.inf
         o[s:s + row_block] = out
@@ -222,19 +236,14 @@ def attention_fp8kv_ref(q, k_codes, v_codes, k_scale: float, v_scale: float, cau
 
 
 def softmax_weights(scores: np.ndarray) -> np.ndarray:
-    """Row softmax of a score matrix (-inf entries get weight 0), float64, two-pass."""
-    s = np.asarray(scores, dtype=np.float64)
-    m = s.max(axis=-1, keepdims=True)
-    m = np.where(np.isfinite(m), m, 0.0)
-    p = np.exp(s - m)
-    return p / p.sum(axis=-1, keepdims=True)
-
-
-def attention_flops(N_q: int, n: int, d: int, causal: bool) -> int:
-    """Algorithmic FLOPs for one query head: 2d for Q.K and 2d for P.V per visible pair."""
-    return 4 * d * visible_pairs(N_q, n, causal)
+    """Row softmax of a score matrix, float64: p / l from softmax_stats. -inf
+    entries get weight 0; a row with no finite entry gets all zeros."""
+    p, _, l = softmax_stats(scores)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        w = p / l[..., None]
+    return np.where(l[..., None] > 0.0, w, 0.0)
 
 
 __all__ = ["score_bytes", "kv_cache_bytes", "visible_pairs", "attention_ref", "attention_head_rows",
            "gather_paged", "attention_paged_ref", "e4m3_value", "dequant_e4m3", "attention_fp8kv_ref",
-           "softmax_weights", "attention_flops", "MiB"]
+           "softmax_stats", "softmax_weights", "MiB"]

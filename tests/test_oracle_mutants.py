@@ -24,9 +24,10 @@ MUTANTS = {
     "top-left causal alignment": ("off = n - N_q", "off = 0"),
     "wrong GQA head map": ("g = h // G", "g = h % H_kv"),
     "V used for scores": ("scores = (qq @ kk.T)", "scores = (qq @ vv.T)"),
-    "no max subtraction": ("p = np.exp(scores - m_safe[:, None])", "p = np.exp(scores)"),
+    "no max subtraction": ("p = np.exp(s - m[..., None])", "p = np.exp(s)"),
+    "max over the wrong axis": ("m = s.max(axis=-1)", "m = s.max(axis=0)"),
     "unnormalised output": ("out = (p @ vv) / l[:, None]", "out = (p @ vv)"),
-    "lse sign": ("row_lse = m_safe + np.log(l)", "row_lse = m_safe - np.log(l)"),
+    "lse sign": ("row_lse = m + np.log(l)", "row_lse = m - np.log(l)"),
     "kv_lens ignored": ("n = N_kv if kv_lens is None else int(kv_lens[b])", "n = N_kv"),
     "empty rows not zeroed": ("out[empty] = 0.0", "pass"),
 }

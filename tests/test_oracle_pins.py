@@ -230,6 +230,87 @@ def test_decode_equals_last_row_of_causal_prefill():
         np.testing.assert_allclose(ld[b, :, 0], lp[0, :, -1], atol=1e-14)
 
 
+def _softmax_python(row):
+    """Softmax of one row in pure Python, written as w_i = 1 / sum_j exp(s_j - s_i)
+    (no maximum taken; exact for rows whose entries differ by far less than 700)."""
+    fin = [x for x in row if x != -math.inf]
+    out = []
+    for x in row:
+        out.append(0.0 if x == -math.inf else 1.0 / math.fsum(math.exp(y - x) for y in fin))
+    return out
+
+
+def test_softmax_matches_pure_python_closed_form():
+    s = rng.standard_normal((6, 11)) * 8
+    s[2, 5:] = -np.inf
+    s[4, :1] = -np.inf
+    w = oracle.softmax_weights(s)
+    for i in range(s.shape[0]):
+        np.testing.assert_allclose(w[i], _softmax_python(list(s[i])), rtol=1e-13, atol=1e-300)
+    # two entries: the logistic function of their difference
+    a, b = 1.7, -0.4
+    w2 = oracle.softmax_weights(np.array([[a, b]]))[0]
+    assert abs(w2[0] - 1.0 / (1.0 + math.exp(b - a))) < 1e-15
+    assert abs(w2[1] - 1.0 / (1.0 + math.exp(a - b))) < 1e-15
+
+
+def test_softmax_invariant_to_row_offsets_beyond_exp_range():
+    """auturnal.com guide, section 8: subtracting the maximum changes only the
+    representation. Offsets of +-800 put every exp(s) outside float64's range
+    (exp(800) overflows, exp(-800) underflows to 0), so only a softmax that
+    subtracts the row maximum returns the same weights."""
+    s = rng.standard_normal((5, 9)) * 10
+    s[1, 3:] = -np.inf
+    w = oracle.softmax_weights(s)
+    for c in (800.0, -800.0, 1e5):
+        wc = oracle.softmax_weights(s + c)
+        assert np.all(np.isfinite(wc))
+        np.testing.assert_allclose(wc, w, rtol=0, atol=1e-10)
+    p, m, l = oracle.softmax_stats(s + 800.0)
+    np.testing.assert_allclose(m, s.max(axis=1) + 800.0, rtol=1e-15)
+    assert np.all(p <= 1.0) and np.all(l >= 1.0)
+
+
+def test_softmax_rows_without_visible_keys():
+    s = np.full((2, 4), -np.inf)
+    s[1, 2] = 3.0
+    p, m, l = oracle.softmax_stats(s)
+    assert np.all(p[0] == 0) and m[0] == 0 and l[0] == 0
+    assert np.array_equal(oracle.softmax_weights(s), np.array([[0, 0, 0, 0], [0, 0, 1, 0]], float))
+
+
+SOFTMAX_MUTANTS = {
+    "no max subtraction": ("p = np.exp(s - m[..., None])", "p = np.exp(s)"),
+    "max over the wrong axis": ("m = s.max(axis=-1)", "m = s.max(axis=0)"),
+    "sum over the wrong axis": ("return p, m, p.sum(axis=-1)", "return p, m, p.sum(axis=0)"),
+    "minimum instead of maximum": ("m = s.max(axis=-1)", "m = s.min(axis=-1)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SOFTMAX_MUTANTS))
+def test_softmax_pins_catch_planted_mistakes(name):
+    import types
+    src = open(oracle.attention.__file__).read()
+    old, new = SOFTMAX_MUTANTS[name]
+    assert src.count(old) == 1, name
+    mod = types.ModuleType("softmax_mutant")
+    exec(compile(src.replace(old, new), "softmax_mutant", "exec"), mod.__dict__)
+    ok = True
+    with np.errstate(all="ignore"):
+        try:
+            saved = oracle.softmax_weights, oracle.softmax_stats
+            oracle.softmax_weights, oracle.softmax_stats = mod.softmax_weights, mod.softmax_stats
+            try:
+                test_softmax_matches_pure_python_closed_form()
+                test_softmax_invariant_to_row_offsets_beyond_exp_range()
+                test_softmax_rows_without_visible_keys()
+            finally:
+                oracle.softmax_weights, oracle.softmax_stats = saved
+        except Exception:  # noqa: BLE001 (a failed assertion or a shape error)
+            ok = False
+    assert not ok, f"mutant {name!r} passed the softmax pins"
+
+
 def test_invariants_weights_hull_permutation():
     s = rng.standard_normal((5, 9)) * 10
     s[1, 3:] = -np.inf
