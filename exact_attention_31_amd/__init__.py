@@ -102,6 +102,13 @@ def _check_tensor(name, t, dtype, device, ndim=4):
         raise ValueError(f"{name} must be a contiguous {ndim}-D tensor")
 
 
+def _check_lse(lse, B, H_q, N_q, device):
+    """lse: float32 [B, H_q, N_q] (the library writes B*H_q*N_q floats through it)."""
+    _check_tensor("lse", lse, torch.float32, device, ndim=3)
+    if tuple(lse.shape) != (B, H_q, N_q):
+        raise ValueError(f"lse is {tuple(lse.shape)}, must be [B, H_q, N_q] = {(B, H_q, N_q)}")
+
+
 def attn_prefill_fwd(q, k, v, o=None, lse=None, *, causal: bool = False, scale: float | None = None,
                      return_lse: bool = False, stream=None):
     """O = softmax(scale * Q K^T) V on the GPU (q [B,H_q,N_q,d], k/v [B,H_kv,N_kv,d]).
@@ -127,9 +134,7 @@ def attn_prefill_fwd(q, k, v, o=None, lse=None, *, causal: bool = False, scale: 
     if lse is None and return_lse:
         lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=dev)
     if lse is not None:
-        _check_tensor("lse", lse, torch.float32, dev, ndim=3)
-        if tuple(lse.shape) != (B, H_q, N_q):
-            raise ValueError("lse must be [B, H_q, N_q]")
+        _check_lse(lse, B, H_q, N_q, dev)
     if scale is None:
         scale = d ** -0.5
     with torch.cuda.device(dev):
@@ -174,7 +179,7 @@ def attn_decode_fwd(q, k_cache, v_cache, o=None, *, kv_lens=None, lse=None, caus
     if lse is None and return_lse:
         lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=dev)
     if lse is not None:
-        _check_tensor("lse", lse, torch.float32, dev, ndim=3)
+        _check_lse(lse, B, H_q, N_q, dev)
     need = attn_decode_workspace_size(B, H_q, H_kv, N_q, N_kv, d, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -228,7 +233,7 @@ def attn_decode_paged_fwd(q, k_pool, v_pool, block_table, o=None, *, kv_lens=Non
     if lse is None and return_lse:
         lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=dev)
     if lse is not None:
-        _check_tensor("lse", lse, torch.float32, dev, ndim=3)
+        _check_lse(lse, B, H_q, N_q, dev)
     need = attn_decode_paged_workspace_size(B, H_q, H_kv, N_q, max_blocks, block_size, d, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -283,7 +288,7 @@ def attn_decode_fp8_fwd(q, k_cache, v_cache, k_scale: float, v_scale: float, o=N
     if lse is None and return_lse:
         lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=dev)
     if lse is not None:
-        _check_tensor("lse", lse, torch.float32, dev, ndim=3)
+        _check_lse(lse, B, H_q, N_q, dev)
     need = attn_decode_workspace_size(B, H_q, H_kv, N_q, N_kv, d, ATTN_BF16)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -330,7 +335,7 @@ def attn_decode_paged_fp8_fwd(q, k_pool, v_pool, k_scale: float, v_scale: float,
     if lse is None and return_lse:
         lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=dev)
     if lse is not None:
-        _check_tensor("lse", lse, torch.float32, dev, ndim=3)
+        _check_lse(lse, B, H_q, N_q, dev)
     need = attn_decode_paged_workspace_size(B, H_q, H_kv, N_q, max_blocks, block_size, d, ATTN_BF16)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -364,15 +369,13 @@ def attn_backward(q, k, v, o, d_o, lse, dq=None, dk=None, dv=None, *, causal: bo
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("d_o", d_o)):
         _check_tensor(name, t, q.dtype, dev)
-    _check_tensor("lse", lse, torch.float32, dev, ndim=3)
     B, H_q, N_q, d = q.shape
+    _check_lse(lse, B, H_q, N_q, dev)
     _, H_kv, N_kv, _ = k.shape
     if tuple(k.shape) != (B, H_kv, N_kv, d) or tuple(v.shape) != tuple(k.shape):
         raise ValueError("k/v shapes do not match q")
     if tuple(o.shape) != tuple(q.shape) or tuple(d_o.shape) != tuple(q.shape):
         raise ValueError("o and d_o must have q's shape")
-    if tuple(lse.shape) != (B, H_q, N_q):
-        raise ValueError("lse must be [B, H_q, N_q]")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
