@@ -69,6 +69,10 @@ def load() -> ctypes.CDLL:
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
     lib.attn_version.restype = i
+    lib.attn_set_tuning.argtypes = [i, i]
+    lib.attn_set_tuning.restype = i
+    lib.attn_get_tuning.argtypes = [i]
+    lib.attn_get_tuning.restype = i
     _lib = lib
     return lib
 
@@ -79,6 +83,44 @@ def attn_status_string(status: int) -> str:
 
 def attn_version() -> int:
     return load().attn_version()
+
+
+TUNING_KNOBS = {"prefill_variant": 0, "prefill_slots": 1, "decode_chunk": 2, "decode_groups": 3,
+                "decode_rows_mode": 4}
+
+
+def set_tuning(name: str, value: int) -> int:
+    """Set a process-wide tuning knob of the library (0 = automatic); returns the old value."""
+    lib = load()
+    knob = TUNING_KNOBS[name]
+    old = lib.attn_get_tuning(knob)
+    st = lib.attn_set_tuning(knob, int(value))
+    if st != 0:
+        raise AttnError(st, f"attn_set_tuning({name}={value})")
+    return old
+
+
+def get_tuning(name: str) -> int:
+    return load().attn_get_tuning(TUNING_KNOBS[name])
+
+
+class tuning:
+    """Context manager that sets tuning knobs and restores them on exit:
+    `with tuning(decode_chunk=2048): ...`."""
+
+    def __init__(self, **knobs):
+        self.knobs = knobs
+        self.saved = {}
+
+    def __enter__(self):
+        for name, value in self.knobs.items():
+            self.saved[name] = set_tuning(name, value)
+        return self
+
+    def __exit__(self, *exc):
+        for name, value in self.saved.items():
+            set_tuning(name, value)
+        return False
 
 
 def _ptr(t):
@@ -402,4 +444,4 @@ def attn_backward(q, k, v, o, d_o, lse, dq=None, dk=None, dv=None, *, causal: bo
 __all__ = ["attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_size",
            "attn_decode_paged_fwd", "attn_decode_paged_workspace_size", "attn_decode_fp8_fwd",
            "attn_decode_paged_fp8_fwd", "attn_backward", "attn_backward_workspace_size", "attn_status_string",
-           "attn_version", "load", "AttnError", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]
+           "attn_version", "set_tuning", "get_tuning", "tuning", "TUNING_KNOBS", "load", "AttnError", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

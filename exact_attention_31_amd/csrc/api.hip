@@ -4,7 +4,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "../../include/attn.h"
 #include "attn_launch.h"
@@ -42,6 +45,51 @@ int check_device() {
   return g_dev_ok[dev] == 1 ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
 }
 
+// ---- tuning knobs: defaults from ATTN_TUNING ("name=value,name=value"), read
+// once per process; attn_set_tuning changes them afterwards.
+std::atomic<int> g_tune[attn::kTuneCount];
+std::once_flag g_tune_once;
+const char* const kTuneNames[attn::kTuneCount] = {"prefill_variant", "prefill_slots", "decode_chunk",
+                                                  "decode_groups", "decode_rows_mode"};
+
+bool tune_valid(int knob, long v) {
+  switch (knob) {
+    case attn::kTunePrefillVariant: return v >= 0 && v <= 5;
+    case attn::kTunePrefillSlots: return v >= 0 && v <= (1L << 20);
+    case attn::kTuneDecodeChunk: return v >= 0 && v <= (1L << 24);
+    case attn::kTuneDecodeGroups: return v == 0 || v == 1 || v == 2 || v == 4;
+    case attn::kTuneDecodeRowsMode: return v >= 0 && v <= 2;
+    default: return false;
+  }
+}
+
+void tune_init() {
+  const char* e = getenv("ATTN_TUNING");
+  if (e == nullptr) return;
+  // entries that do not parse, name no knob or hold an invalid value are ignored
+  while (*e) {
+    const char* end = strchr(e, ',');
+    const size_t n = end ? (size_t)(end - e) : strlen(e);
+    const char* eq = (const char*)memchr(e, '=', n);
+    if (eq != nullptr) {
+      for (int k = 0; k < attn::kTuneCount; ++k) {
+        const size_t kl = strlen(kTuneNames[k]);
+        if ((size_t)(eq - e) == kl && strncmp(e, kTuneNames[k], kl) == 0) {
+          char* stop = nullptr;
+          const long v = strtol(eq + 1, &stop, 10);
+          if (stop == e + n && stop != eq + 1 && tune_valid(k, v)) g_tune[k].store((int)v);
+        }
+      }
+    }
+    e += n;
+    if (*e == ',') ++e;
+  }
+}
+
+// ---- occupancy per (kernel, device)
+std::map<std::pair<const void*, int>, int> g_occ;
+std::mutex g_occ_mu;
+
 size_t elem_size(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -66,7 +114,43 @@ int check_common(int B, int H_q, int H_kv, int N_q, int N_kv, int d, int dtype, 
 
 }  // namespace
 
+namespace attn {
+
+int tuning(int knob) {
+  std::call_once(g_tune_once, tune_init);
+  return (knob >= 0 && knob < kTuneCount) ? g_tune[knob].load(std::memory_order_relaxed) : 0;
+}
+
+int occupancy_per_cu(const void* kernel, int threads, int device) {
+  std::lock_guard<std::mutex> lk(g_occ_mu);
+  const auto key = std::make_pair(kernel, device);
+  auto it = g_occ.find(key);
+  if (it != g_occ.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = 1;
+  }
+  g_occ[key] = n;
+  return n;
+}
+
+}  // namespace attn
+
 extern "C" {
+
+int attn_set_tuning(int knob, int value) {
+  if (knob < 0 || knob >= attn::kTuneCount) return ATTN_ERR_VALUE;
+  if (!tune_valid(knob, value)) return ATTN_ERR_VALUE;
+  std::call_once(g_tune_once, tune_init);
+  g_tune[knob].store(value, std::memory_order_relaxed);
+  return ATTN_OK;
+}
+
+int attn_get_tuning(int knob) {
+  if (knob < 0 || knob >= attn::kTuneCount) return -1;
+  return attn::tuning(knob);
+}
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -113,7 +197,8 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
   if (st != ATTN_OK) return st;
   int dev = 0;
   (void)hipGetDevice(&dev);
-  attn::PrefillArgs a{q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale, dtype, g_dev_cus[dev]};
+  attn::PrefillArgs a{q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale, dtype, g_dev_cus[dev],
+                      dev};
   return attn::launch_prefill(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -194,18 +279,19 @@ int decode_launch(const void* q, const void* k, const void* v, size_t kv_bytes, 
   // Many query rows per KV head (G * N_q, several new tokens) and enough
   // of them to fill the device: the rows are a tall product, better served by
   // the prefill kernel in rows mode (32x32 MFMA tiles, K/V shared through LDS)
-  // than by the split-KV decode kernel. ATTN_DECODE_ROWS_MODE = 0 / 1 forces it
-  // off / on (contiguous 16-bit caches only).
+  // than by the split-KV decode kernel. The decode_rows_mode knob forces it
+  // on (1) or off (2) (contiguous 16-bit caches only).
   if (!paged && !kv_fp8) {
     const int rows = (H_q / H_kv) * N_q;
     const int bm = d == 128 ? 256 : 128;  // query rows per prefill workgroup
     const int64_t items = (int64_t)B * H_kv * ((rows + bm - 1) / bm);
     // at least half a workgroup's rows (padding rows cost as much as real ones)
     bool rows_mode = 2 * rows >= bm && items >= (g_dev_cus[dev] > 0 ? g_dev_cus[dev] : 256);
-    if (const char* e = getenv("ATTN_DECODE_ROWS_MODE")) rows_mode = atoi(e) != 0;
+    const int forced = attn::tuning(attn::kTuneDecodeRowsMode);
+    if (forced != 0) rows_mode = forced == 1;
     if (rows_mode) {
       attn::PrefillArgs pa{q, k, v, o, lse, B, H_kv, H_kv, rows, N_kv, d, causal, scale, dtype,
-                           g_dev_cus[dev]};
+                           g_dev_cus[dev], dev};
       return attn::launch_prefill_rows(pa, kv_lens, N_q, (hipStream_t)stream) == hipSuccess
                  ? ATTN_OK
                  : ATTN_ERR_LAUNCH;

@@ -5,7 +5,40 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace attn {
+
+// Tuning knobs (attn_set_tuning, or the ATTN_TUNING environment variable read
+// once per process). Never needed for correctness: every setting gives the
+// same results up to rounding. 0 = automatic.
+enum TuneKnob {
+  kTunePrefillVariant = 0,  // 1..5: alternative prefill kernel forms
+  kTunePrefillSlots = 1,    // n > 0: persistent prefill grid with at most n workgroups
+  kTuneDecodeChunk = 2,     // n > 0: keys per decode split (rounded up to 128), no device raise
+  kTuneDecodeGroups = 3,    // 1, 2 or 4: query column groups per decode wavefront
+  kTuneDecodeRowsMode = 4,  // 1: multi-token decode through the prefill kernel; 2: never
+  kTuneCount = 5
+};
+int tuning(int knob);
+
+// Resident workgroups of `kernel` (launched with `threads` threads) per compute
+// unit of device `device`, cached per (kernel, device).
+int occupancy_per_cu(const void* kernel, int threads, int device);
+
+// Launches `kernel` with `args` converted to its parameter types and returns
+// the status of this launch alone (no earlier error is picked up).
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, A... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> vals{static_cast<P>(args)...};
+  return std::apply(
+      [&](auto&... v) {
+        void* ptrs[] = {(void*)&v...};
+        return hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, stream);
+      },
+      vals);
+}
 
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeF16 = 1;
@@ -22,6 +55,7 @@ struct PrefillArgs {
   float scale;
   int dtype;
   int num_cus;  // compute units of the device (sizes persistent grids)
+  int device;   // HIP device index (occupancy cache)
 };
 
 struct DecodeArgs {

@@ -559,44 +559,39 @@ template <class TT, int D>
 hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.H_q * a.N_q;
   const float sl2 = a.scale * kLog2e;
+  const auto q = (const uint16_t*)a.q;
+  const auto k = (const uint16_t*)a.k;
+  const auto v = (const uint16_t*)a.v;
+  const auto d_o = (const uint16_t*)a.d_o;
   if (rows > 0) {
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st,
-                       (const uint16_t*)a.o, (const uint16_t*)a.d_o, a.lse, a.lse2, a.delta, rows,
-                       a.dtype == kDtypeBF16);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = launch_kernel(bwd_prep_kernel<D>, dim3((unsigned)((rows + 15) / 16)), dim3(256), st,
+                                       (const uint16_t*)a.o, d_o, a.lse, a.lse2, a.delta, rows,
+                                       a.dtype == kDtypeBF16);
     if (e != hipSuccess) return e;
   }
   if (a.N_kv > 0) {
     const int nkb = (a.N_kv + kBwdKW - 1) / kBwdKW;
-    const unsigned g = xcd_grid((int64_t)nkb * a.H_kv * a.B);
-    if (a.causal)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, true>), dim3(g), dim3(64 * kBwdNWK), 0, st,
-                         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                         (const uint16_t*)a.d_o, a.lse2, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                         a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, a.scale, nkb, a.B);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, false>), dim3(g), dim3(64 * kBwdNWK), 0, st,
-                         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                         (const uint16_t*)a.d_o, a.lse2, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                         a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, a.scale, nkb, a.B);
-    hipError_t e = hipGetLastError();
+    const dim3 g(xcd_grid((int64_t)nkb * a.H_kv * a.B));
+    const hipError_t e =
+        a.causal ? launch_kernel(bwd_dkdv_kernel<TT, D, true>, g, dim3(64 * kBwdNWK), st, q, k, v, d_o,
+                                 a.lse2, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H_q, a.H_kv, a.N_q,
+                                 a.N_kv, sl2, a.scale, nkb, a.B)
+                 : launch_kernel(bwd_dkdv_kernel<TT, D, false>, g, dim3(64 * kBwdNWK), st, q, k, v, d_o,
+                                 a.lse2, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H_q, a.H_kv, a.N_q,
+                                 a.N_kv, sl2, a.scale, nkb, a.B);
     if (e != hipSuccess) return e;
   }
   if (a.N_q > 0) {
     constexpr int NW = 8;  // 256 rows per workgroup, two wavefronts per SIMD
     const int nqb = (a.N_q + 32 * NW - 1) / (32 * NW);
-    const unsigned g = xcd_grid((int64_t)nqb * a.H_q * a.B);
-    if (a.causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<TT, D, true, NW>), dim3(g), dim3(64 * NW), 0, st,
-                         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                         (const uint16_t*)a.d_o, a.lse2, a.delta, (uint16_t*)a.dq, a.H_q, a.H_kv,
-                         a.N_q, a.N_kv, sl2, a.scale, nqb, a.B);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<TT, D, false, NW>), dim3(g), dim3(64 * NW), 0, st,
-                         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                         (const uint16_t*)a.d_o, a.lse2, a.delta, (uint16_t*)a.dq, a.H_q, a.H_kv,
-                         a.N_q, a.N_kv, sl2, a.scale, nqb, a.B);
-    hipError_t e = hipGetLastError();
+    const dim3 g(xcd_grid((int64_t)nqb * a.H_q * a.B));
+    const hipError_t e =
+        a.causal ? launch_kernel(bwd_dq_kernel<TT, D, true, NW>, g, dim3(64 * NW), st, q, k, v, d_o, a.lse2,
+                                 a.delta, (uint16_t*)a.dq, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, a.scale, nqb,
+                                 a.B)
+                 : launch_kernel(bwd_dq_kernel<TT, D, false, NW>, g, dim3(64 * NW), st, q, k, v, d_o, a.lse2,
+                                 a.delta, (uint16_t*)a.dq, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, a.scale, nqb,
+                                 a.B);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

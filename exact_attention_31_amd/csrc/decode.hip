@@ -534,31 +534,26 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   P.chunk = a.chunk;
   P.chunk_cap = a.chunk_cap;
   P.scale_log2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
-  if (a.block_table != nullptr)
-    hipLaunchKernelGGL((decode_split_kernel<TT, D, NG, OCC, true, FP8>), grid, dim3(kThreads), 0, st, P);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<TT, D, NG, OCC, false, FP8>), grid, dim3(kThreads), 0, st, P);
-  hipError_t e = hipGetLastError();
+  const hipError_t e =
+      a.block_table != nullptr
+          ? launch_kernel(decode_split_kernel<TT, D, NG, OCC, true, FP8>, grid, dim3(kThreads), st, P)
+          : launch_kernel(decode_split_kernel<TT, D, NG, OCC, false, FP8>, grid, dim3(kThreads), st, P);
   if (e != hipSuccess) return e;
   const int BH = a.B * a.H_q * a.N_q;
-  hipLaunchKernelGGL((decode_merge_kernel<TT, D>), dim3((BH + 3) / 4), dim3(256), 0, st, a.part_u,
-                     a.part_ml, a.kv_lens, (uint16_t*)a.o, a.lse, a.H_q * a.N_q, a.N_kv, a.splits,
-                     a.chunk, a.chunk_cap, a.H_kv * ngroups, (int)grid.x * 4, BH,
-                     FP8 ? a.v_scale : 1.f);
-  return hipGetLastError();
+  return launch_kernel(decode_merge_kernel<TT, D>, dim3((BH + 3) / 4), dim3(256), st, a.part_u,
+                       a.part_ml, a.kv_lens, (uint16_t*)a.o, a.lse, a.H_q * a.N_q, a.N_kv, a.splits,
+                       a.chunk, a.chunk_cap, a.H_kv * ngroups, (int)grid.x * 4, BH,
+                       FP8 ? a.v_scale : 1.f);
 }
 
 template <class TT, bool FP8>
 hipError_t launch_dtype(const DecodeArgs& a, hipStream_t st) {
   // more than 16 query rows per KV head: each wavefront serves two or four
   // column groups, so K and V are read once per 32 or 64 rows
-  // (ATTN_DECODE_GROUPS = 1, 2 or 4 forces a choice)
+  // (the decode_groups knob forces 1, 2 or 4)
   const int cols = (a.H_q / a.H_kv) * a.N_q;
   int ng = cols <= kQCols ? 1 : (cols <= 2 * kQCols ? 2 : 4);
-  if (const char* e = getenv("ATTN_DECODE_GROUPS")) {
-    const int f = atoi(e);
-    if (f == 1 || f == 2 || f == 4) ng = f;
-  }
+  if (const int f = tuning(kTuneDecodeGroups)) ng = f;
   if (a.d == 64) {
     if (ng == 1) return launch_t<TT, 64, 1, 2, FP8>(a, st);
     return ng == 2 ? launch_t<TT, 64, 2, 2, FP8>(a, st) : launch_t<TT, 64, 4, 2, FP8>(a, st);
@@ -583,11 +578,10 @@ DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool 
   // caches keep at most 2048 keys per chunk, whose block-table entries sit in
   // one register pair per lane.
   int64_t cap = paged ? 2048 : ((int64_t)N_kv + kStepKeys - 1) / kStepKeys * kStepKeys;
-  // tuning override (keys per split, rounded up to a multiple of 128, used as
-  // given: no raise on the device)
-  if (const char* e = getenv("ATTN_DECODE_CHUNK")) {
-    const long v = strtol(e, nullptr, 10);
-    if (v > 0 && v <= (1L << 24)) chunk = ((v + kStepKeys - 1) / kStepKeys) * kStepKeys;
+  // tuning override (the decode_chunk knob: keys per split, rounded up to a
+  // multiple of 128, used as given: no raise on the device)
+  if (const int v = tuning(kTuneDecodeChunk)) {
+    chunk = ((v + kStepKeys - 1) / kStepKeys) * kStepKeys;
     if (paged && chunk > 2048) chunk = 2048;
     cap = chunk;
   }

@@ -29,8 +29,6 @@
 //   * exp is evaluated as exp2 with scale*log2(e) folded into one multiply.
 // fp32 inputs use v_mfma_f32_32x32x2_f32 in the same arrangement (no LDS
 // transpose is needed there because each lane feeds one K-slot).
-#include <stdlib.h>
-
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -937,11 +935,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill32_kernel(
 // 1-D grid covering `items` work items, rounded up to a multiple of the 8 XCDs.
 inline int xcd_grid(int64_t items) { return (int)(((items + 7) / 8) * 8); }
 
-// Persistent launch of the default kernel: one workgroup per resident slot
-// (occupancy from the runtime, times the compute units), at most one per item.
-// With fewer than four items per slot the static zig-zag cannot balance
-// causal items of very different lengths, and the hardware's dynamic dispatch
-// of one item per workgroup does better; the persistent grid is used above that.
 // Which form of the default kernel runs: the ring form for d = 64, the
 // register-staged form for d = 128 (measured on the two shapes' workloads; at
 // d = 128 the two are within noise of each other).
@@ -955,36 +948,27 @@ constexpr auto prefill16_form() {
     return prefill16_kernel<TT, D, CAUSAL, 1, NW, PERSIST>;
 }
 
+// Persistent launch of the default kernel: one workgroup per resident slot
+// (occupancy from the runtime, times the compute units), at most one per item.
+// With fewer than four items per slot the static zig-zag cannot balance
+// causal items of very different lengths, and the hardware's dynamic dispatch
+// of one item per workgroup does better; the persistent grid is used above that.
 template <class TT, int D, int NW, bool CAUSAL, bool RING>
-hipError_t launch16pers_t(const PrefillArgs& a, hipStream_t st, int nqb, const int* kv_lens = nullptr,
-                          int row_period = 0) {
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill16_form<TT, D, CAUSAL, NW, true, RING>(),
-                                                     64 * NW, 0) != hipSuccess || n < 1)
-      n = 1;
-    per_cu = n;
-  }
+hipError_t launch16pers_t(const PrefillArgs& a, hipStream_t st, int nqb, const int* kv_lens,
+                          int row_period) {
+  constexpr auto kpers = prefill16_form<TT, D, CAUSAL, NW, true, RING>();
+  constexpr auto kone = prefill16_form<TT, D, CAUSAL, NW, false, RING>();
+  const int per_cu = occupancy_per_cu((const void*)kpers, 64 * NW, a.device);
   const int64_t items = (int64_t)nqb * a.H_q * a.B;
   int64_t slots = (int64_t)per_cu * (a.num_cus > 0 ? a.num_cus : 256);
-  // tuning and testing: ATTN_PREFILL_SLOTS = n forces the persistent grid with n slots
-  const char* env = getenv("ATTN_PREFILL_SLOTS");
-  const int64_t forced = env ? atol(env) : 0;
+  // tuning and testing: the prefill_slots knob forces the persistent grid with n slots
+  const int64_t forced = tuning(kTunePrefillSlots);
   if (forced > 0) slots = forced < slots ? forced : slots;
   const float sl2 = a.scale * kLog2e;
-  if (forced <= 0 && items < 4 * slots) {
-    hipLaunchKernelGGL((prefill16_form<TT, D, CAUSAL, NW, false, RING>()), dim3(xcd_grid(items)),
-                       dim3(64 * NW), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2,
-                       nqb, a.B, kv_lens, row_period);
-  } else {
-    hipLaunchKernelGGL((prefill16_form<TT, D, CAUSAL, NW, true, RING>()), dim3(xcd_grid(slots)),
-                       dim3(64 * NW), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2,
-                       nqb, a.B, kv_lens, row_period);
-  }
-  return hipGetLastError();
+  const bool pers = forced > 0 || items >= 4 * slots;
+  return launch_kernel(pers ? kpers : kone, dim3(xcd_grid(pers ? slots : items)), dim3(64 * NW), st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                       a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B, kv_lens, row_period);
 }
 
 template <class TT, int D, int NW, bool RING = false>
@@ -999,25 +983,18 @@ template <class TT, int D, int QB, int NW = 4>
 hipError_t launch16q(const PrefillArgs& a, hipStream_t st) {
   constexpr int BM = NW * 32 * QB;
   const int nqb = (a.N_q + BM - 1) / BM;
-  dim3 grid(xcd_grid((int64_t)nqb * a.H_q * a.B));
+  const dim3 grid(xcd_grid((int64_t)nqb * a.H_q * a.B));
   const float sl2 = a.scale * kLog2e;
-  auto q = (const uint16_t*)a.q;
-  auto k = (const uint16_t*)a.k;
-  auto v = (const uint16_t*)a.v;
-  auto o = (uint16_t*)a.o;
-  if (a.causal)
-    hipLaunchKernelGGL((prefill16_kernel<TT, D, true, QB, NW>), grid, dim3(64 * NW), 0, st, q, k, v,
-                       o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
-  else
-    hipLaunchKernelGGL((prefill16_kernel<TT, D, false, QB, NW>), grid, dim3(64 * NW), 0, st, q, k, v,
-                       o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb, a.B);
-  return hipGetLastError();
+  const auto kern = a.causal ? prefill16_kernel<TT, D, true, QB, NW> : prefill16_kernel<TT, D, false, QB, NW>;
+  return launch_kernel(kern, grid, dim3(64 * NW), st, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb,
+                       a.B, (const int*)nullptr, 0);
 }
 
 // Kernel form for 16-bit inputs: one 32-row query block per wavefront, 8
 // wavefronts (256 rows) per workgroup for d = 128 and 4 (128 rows) for d = 64,
 // where the smaller register footprint buys a third resident wavefront per
-// SIMD instead. ATTN_PREFILL_VARIANT selects alternative forms (tuning and
+// SIMD instead. The prefill_variant knob selects alternative forms (tuning and
 // testing only): 1 = 4 wavefronts per workgroup, one work item each; 2 = two
 // query blocks per wavefront; 3 = the default wavefront count with one work
 // item per workgroup instead of a persistent grid; 4 = the ring form (direct
@@ -1025,8 +1002,7 @@ hipError_t launch16q(const PrefillArgs& a, hipStream_t st) {
 template <class TT, int D>
 hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
   constexpr int NW = (D == 128) ? 8 : 4;
-  const char* env = getenv("ATTN_PREFILL_VARIANT");
-  const int variant = env ? atoi(env) : 0;
+  const int variant = tuning(kTunePrefillVariant);
   if (variant == 1) return launch16q<TT, D, 1, 4>(a, st);
   if (variant == 2) return launch16q<TT, D, 2>(a, st);
   if (variant == 3) return launch16q<TT, D, 1, NW>(a, st);
@@ -1038,19 +1014,22 @@ hipError_t launch16(const PrefillArgs& a, hipStream_t st) {
 template <int D>
 hipError_t launch32(const PrefillArgs& a, hipStream_t st) {
   const int nqb = (a.N_q + kBM - 1) / kBM;
-  dim3 grid(nqb, a.H_q, a.B);
+  const dim3 grid(nqb, a.H_q, a.B);
   const float sl2 = a.scale * kLog2e;
-  auto q = (const float*)a.q;
-  auto k = (const float*)a.k;
-  auto v = (const float*)a.v;
-  auto o = (float*)a.o;
-  if (a.causal)
-    hipLaunchKernelGGL((prefill32_kernel<D, true>), grid, dim3(kThreads), 0, st, q, k, v, o, a.lse,
-                       a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb);
-  else
-    hipLaunchKernelGGL((prefill32_kernel<D, false>), grid, dim3(kThreads), 0, st, q, k, v, o, a.lse,
-                       a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb);
-  return hipGetLastError();
+  const auto kern = a.causal ? prefill32_kernel<D, true> : prefill32_kernel<D, false>;
+  return launch_kernel(kern, grid, dim3(kThreads), st, (const float*)a.q, (const float*)a.k,
+                       (const float*)a.v, (float*)a.o, a.lse, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, nqb);
+}
+
+// Rows mode at either head dim: the ring or the staged form (the default form
+// unless the prefill_variant knob is 4 or 5).
+template <class TT, int D>
+hipError_t launch_rows16(const PrefillArgs& a, const int* kv_lens, int row_period, hipStream_t st) {
+  constexpr int NW = (D == 128) ? 8 : 4;
+  const int variant = tuning(kTunePrefillVariant);
+  const bool ring = variant == 4 ? true : variant == 5 ? false : kRingDefault<D>;
+  return ring ? launch16pers<TT, D, NW, true>(a, st, kv_lens, row_period)
+              : launch16pers<TT, D, NW, false>(a, st, kv_lens, row_period);
 }
 
 }  // namespace
@@ -1059,25 +1038,11 @@ hipError_t launch32(const PrefillArgs& a, hipStream_t st) {
 // lengths; see prefill16_kernel).
 hipError_t launch_prefill_rows(const PrefillArgs& a, const int* kv_lens, int row_period,
                                hipStream_t st) {
-  const char* env = getenv("ATTN_PREFILL_VARIANT");
-  const int variant = env ? atoi(env) : 0;
-  if (variant == 4 || variant == 5) {  // tuning and testing: force the ring or the staged form
-    const bool ring = variant == 4;
-    if (a.dtype == kDtypeBF16)
-      return a.d == 64 ? (ring ? launch16pers<BF16, 64, 4, true>(a, st, kv_lens, row_period)
-                               : launch16pers<BF16, 64, 4, false>(a, st, kv_lens, row_period))
-                       : (ring ? launch16pers<BF16, 128, 8, true>(a, st, kv_lens, row_period)
-                               : launch16pers<BF16, 128, 8, false>(a, st, kv_lens, row_period));
-    return a.d == 64 ? (ring ? launch16pers<F16, 64, 4, true>(a, st, kv_lens, row_period)
-                             : launch16pers<F16, 64, 4, false>(a, st, kv_lens, row_period))
-                     : (ring ? launch16pers<F16, 128, 8, true>(a, st, kv_lens, row_period)
-                             : launch16pers<F16, 128, 8, false>(a, st, kv_lens, row_period));
-  }
   if (a.dtype == kDtypeBF16)
-    return a.d == 64 ? launch16pers<BF16, 64, 4, kRingDefault<64>>(a, st, kv_lens, row_period)
-                     : launch16pers<BF16, 128, 8, kRingDefault<128>>(a, st, kv_lens, row_period);
-  return a.d == 64 ? launch16pers<F16, 64, 4, kRingDefault<64>>(a, st, kv_lens, row_period)
-                   : launch16pers<F16, 128, 8, kRingDefault<128>>(a, st, kv_lens, row_period);
+    return a.d == 64 ? launch_rows16<BF16, 64>(a, kv_lens, row_period, st)
+                     : launch_rows16<BF16, 128>(a, kv_lens, row_period, st);
+  return a.d == 64 ? launch_rows16<F16, 64>(a, kv_lens, row_period, st)
+                   : launch_rows16<F16, 128>(a, kv_lens, row_period, st);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {

@@ -215,6 +215,42 @@ const char* attn_status_string(int status);
 /* Library ABI version (major * 100 + minor). */
 int attn_version(void);
 
+/*
+ * Tuning knobs. No setting is ever needed for correctness: every value gives
+ * the same results up to rounding, and 0 always means "chosen automatically".
+ * Settings are process-wide and apply to calls made after the change (thread
+ * safe: each knob is one atomic integer). Their initial values come from the
+ * environment variable ATTN_TUNING, read once per process at the first call
+ * that needs a knob, as comma-separated name=value pairs with the names below
+ * (e.g. "prefill_variant=4,decode_chunk=2048"); entries that do not parse or
+ * hold an invalid value are ignored.
+ *   ATTN_TUNE_PREFILL_VARIANT  "prefill_variant"  1..5: alternative forms of the
+ *       16-bit prefill kernel (1: 4 wavefronts per workgroup; 2: two query
+ *       blocks per wavefront; 3: one work item per workgroup; 4: direct-to-LDS
+ *       ring form; 5: register-staged form).
+ *   ATTN_TUNE_PREFILL_SLOTS    "prefill_slots"    n > 0: persistent prefill grid
+ *       with at most n workgroups.
+ *   ATTN_TUNE_DECODE_CHUNK     "decode_chunk"     n > 0: keys per decode split
+ *       (rounded up to 128; at most 2048 for paged caches), used as given. The
+ *       decode workspace sizes depend on it.
+ *   ATTN_TUNE_DECODE_GROUPS    "decode_groups"    1, 2 or 4 query column groups
+ *       per decode wavefront.
+ *   ATTN_TUNE_DECODE_ROWS_MODE "decode_rows_mode" 1: multi-token decode of
+ *       contiguous 16-bit caches always through the prefill kernel; 2: never.
+ * attn_set_tuning returns ATTN_ERR_VALUE (and changes nothing) for an unknown
+ * knob or a value outside its range; attn_get_tuning returns the current value,
+ * or -1 for an unknown knob.
+ */
+typedef enum {
+  ATTN_TUNE_PREFILL_VARIANT = 0,
+  ATTN_TUNE_PREFILL_SLOTS = 1,
+  ATTN_TUNE_DECODE_CHUNK = 2,
+  ATTN_TUNE_DECODE_GROUPS = 3,
+  ATTN_TUNE_DECODE_ROWS_MODE = 4
+} attn_tune_t;
+int attn_set_tuning(int knob, int value);
+int attn_get_tuning(int knob);
+
 #ifdef __cplusplus
 }
 #endif

@@ -173,3 +173,39 @@ def test_backward_argument_errors():
     assert bw(ws=None) == 5 and bw(wsb=4) == 5
     assert bw(B=0) == 0
     assert bw() == 7 and bw(Nkv=0) == 7
+
+
+def test_tuning_knobs_set_get_and_reject_invalid_values():
+    for name, knob in E.TUNING_KNOBS.items():
+        assert L.attn_get_tuning(knob) == 0, name      # automatic unless ATTN_TUNING says otherwise
+    assert L.attn_get_tuning(99) == -1 and L.attn_set_tuning(99, 1) == 9
+    bad = {"prefill_variant": [6, -1], "prefill_slots": [-2], "decode_chunk": [-5, 1 << 25],
+           "decode_groups": [3, 8], "decode_rows_mode": [3, -1]}
+    for name, values in bad.items():
+        for v in values:
+            assert L.attn_set_tuning(E.TUNING_KNOBS[name], v) == 9, (name, v)
+            assert E.get_tuning(name) == 0
+    with E.tuning(decode_chunk=700, decode_groups=2):
+        assert E.get_tuning("decode_chunk") == 700 and E.get_tuning("decode_groups") == 2
+    assert E.get_tuning("decode_chunk") == 0 and E.get_tuning("decode_groups") == 0
+
+
+def test_tuning_defaults_come_from_the_environment_once():
+    import subprocess
+    import sys
+    code = ("import exact_attention_31_amd as E; "
+            "print(*[E.get_tuning(n) for n in ('prefill_variant', 'decode_chunk', 'decode_groups', "
+            "'decode_rows_mode', 'prefill_slots')])")
+    env = dict(os.environ, ATTN_TUNING="prefill_variant=4,decode_chunk=2048,decode_groups=3,bogus=1,"
+                                       "decode_rows_mode=2x,prefill_slots=")
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, cwd=ROOT,
+                         check=True).stdout.split()
+    # decode_groups=3 is out of range, "2x" and "" do not parse: those stay automatic
+    assert out == ["4", "2048", "0", "0", "0"]
+
+
+def test_decode_workspace_follows_the_chunk_knob():
+    base = L.attn_decode_workspace_size(2, 8, 2, 1, 4096, 128, E.ATTN_BF16)
+    with E.tuning(decode_chunk=128):
+        fine = L.attn_decode_workspace_size(2, 8, 2, 1, 4096, 128, E.ATTN_BF16)
+    assert fine == 2 * 8 * 1 * (4096 // 128) * 130 * 4 and fine > base

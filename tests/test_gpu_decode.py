@@ -155,19 +155,19 @@ def test_decode_config5_full_size(ragged):
 
 
 @pytest.mark.parametrize("chunk", [128, 384, 1024, 8192])
-def test_decode_split_size_does_not_change_the_result(chunk, monkeypatch):
+def test_decode_split_size_does_not_change_the_result(chunk, tune):
     """The split of the KV sequence is a performance choice only: every split size
     matches the oracle (and so each other) within the tolerance."""
-    monkeypatch.setenv("ATTN_DECODE_CHUNK", str(chunk))
+    tune(decode_chunk=chunk)
     _decode_case(3, 16, 2, 5000, 128, "bf16", [5000, 1, 2600], seed=91)
     _decode_case(2, 8, 2, 3000, 128, "bf16", [3000, 2000], seed=92, Nq=5, causal=True)
 
 
 @pytest.mark.parametrize("groups", ["1", "2", "4"])
-def test_decode_column_groups_per_wavefront_agree(groups, monkeypatch):
+def test_decode_column_groups_per_wavefront_agree(groups, tune):
     """How many 16-column groups one wavefront serves is a performance choice:
     every setting matches the oracle."""
-    monkeypatch.setenv("ATTN_DECODE_GROUPS", groups)
+    tune(decode_groups=groups)
     _decode_case(2, 16, 2, 2100, 128, "bf16", [2100, 999], seed=93, Nq=6, causal=True)
     _decode_case(2, 8, 2, 1100, 64, "f16", [1100, 64], seed=94, Nq=3, causal=True)
 
@@ -175,10 +175,10 @@ def test_decode_column_groups_per_wavefront_agree(groups, monkeypatch):
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("case", MULTI, ids=lambda c: "x".join(map(str, c[:6])))
-def test_decode_rows_mode_matches_oracle(case, dtype, causal, monkeypatch):
+def test_decode_rows_mode_matches_oracle(case, dtype, causal, tune):
     """Multi-token decode through the prefill kernel in rows mode (forced here;
     chosen automatically for many rows per KV head and many KV heads)."""
-    monkeypatch.setenv("ATTN_DECODE_ROWS_MODE", "1")
+    tune(decode_rows_mode=1)
     B, Hq, Hkv, Nkv, d, Nq, lens = case
     _decode_case(B, Hq, Hkv, Nkv, d, dtype, lens,
                  seed=zlib.crc32(repr((case, dtype, causal, "rows")).encode()) % 10000, Nq=Nq,
@@ -193,11 +193,11 @@ def test_decode_rows_mode_chosen_for_tall_batches():
 
 @pytest.mark.parametrize("form", ["4", "5"], ids=["ring", "staged"])
 @pytest.mark.parametrize("case", [MULTI[2], MULTI[4], MULTI[7]], ids=lambda c: "x".join(map(str, c[:6])))
-def test_decode_rows_mode_both_kernel_forms(case, form, monkeypatch):
+def test_decode_rows_mode_both_kernel_forms(case, form, tune):
     """Rows mode through either form of the prefill kernel (K/V tiles streamed
     by direct loads, or staged through registers)."""
-    monkeypatch.setenv("ATTN_DECODE_ROWS_MODE", "1")
-    monkeypatch.setenv("ATTN_PREFILL_VARIANT", form)
+    tune(decode_rows_mode=1)
+    tune(prefill_variant=form)
     B, Hq, Hkv, Nkv, d, Nq, lens = case
     _decode_case(B, Hq, Hkv, Nkv, d, "bf16", lens,
                  seed=zlib.crc32(repr((case, form)).encode()) % 10000, Nq=Nq, causal=True)

@@ -166,22 +166,22 @@ MANY_ITEMS = [(2, 64, 64, 700, 700, 128), (4, 64, 16, 500, 500, 64), (1, 48, 8, 
 @pytest.mark.parametrize("slots", [None, "16", "8"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", MANY_ITEMS, ids=lambda s: "x".join(map(str, s)))
-def test_prefill_persistent_grid_many_items(shape, causal, slots, form, monkeypatch):
+def test_prefill_persistent_grid_many_items(shape, causal, slots, form, tune):
     """Several items per workgroup: a persistent grid of 8 or 16 workgroups (or
     the automatic choice) walks every query block exactly once, with the K/V
     tiles staged through registers or streamed by direct loads across items."""
     if slots is not None:
-        monkeypatch.setenv("ATTN_PREFILL_SLOTS", slots)
+        tune(prefill_slots=slots)
     if form is not None:
-        monkeypatch.setenv("ATTN_PREFILL_VARIANT", form)
+        tune(prefill_variant=form)
     _run_small(*shape, "bf16", causal, seed=zlib.crc32(repr((shape, causal)).encode()) % 10000)
 
 
 @pytest.mark.parametrize("variant", ["1", "2", "3", "4", "5"])
-def test_prefill_variants_match_oracle(variant, monkeypatch):
-    """Every alternative kernel behind ATTN_PREFILL_VARIANT (tuning only) meets
+def test_prefill_variants_match_oracle(variant, tune):
+    """Every alternative kernel behind the prefill_variant knob (tuning only) meets
     the same bar as the default."""
-    monkeypatch.setenv("ATTN_PREFILL_VARIANT", variant)
+    tune(prefill_variant=variant)
     for i, (shape, causal, dtype) in enumerate([
             ((1, 4, 2, 300, 300, 128), True, "bf16"), ((2, 2, 2, 129, 257, 64), True, "f16"),
             ((1, 8, 8, 200, 200, 128), False, "f16"), ((1, 2, 1, 70, 30, 64), True, "bf16")]):
