@@ -49,6 +49,8 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_workspace_size.restype = sz
     lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_decode_fwd.restype = i
+    lib.attn_decode_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.attn_decode_fwd_noalloc.restype = i
     lib.attn_decode_paged_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
     lib.attn_decode_paged_workspace_size.restype = sz
     lib.attn_decode_paged_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i,
@@ -235,6 +237,43 @@ def attn_decode_fwd(q, k_cache, v_cache, o=None, *, kv_lens=None, lse=None, caus
     if st != 0:
         raise AttnError(st, "attn_decode_fwd")
     return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_decode_fwd_noalloc(q, k_cache, v_cache, o, *, kv_lens=None, lse=None, causal: bool = False,
+                            scale: float | None = None, stream=None):
+    """attn_decode_fwd with the split partials in the library's per-device scratch
+    (ATTN_DECODE_SCRATCH_BYTES) instead of a workspace: the library allocates
+    nothing, so o (and lse, if wanted) must be given. Calls that overlap on one
+    device race on the shared scratch."""
+    lib = load()
+    if q.dtype not in DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _check_tensor("q", q, q.dtype, dev)
+    _check_tensor("k_cache", k_cache, q.dtype, dev)
+    _check_tensor("v_cache", v_cache, q.dtype, dev)
+    B, H_q, N_q, d = q.shape
+    _, H_kv, N_kv, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, H_kv, N_kv, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if kv_lens is not None:
+        _check_tensor("kv_lens", kv_lens, torch.int32, dev, ndim=1)
+        if kv_lens.shape[0] != B:
+            raise ValueError("kv_lens must have B entries")
+    _check_tensor("o", o, q.dtype, dev)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape")
+    if lse is not None:
+        _check_lse(lse, B, H_q, N_q, dev)
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(dev):
+        st = lib.attn_decode_fwd_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens), _ptr(o),
+                                         _ptr(lse), B, H_q, H_kv, N_q, N_kv, d, int(bool(causal)),
+                                         float(scale), DTYPE_CODE[q.dtype], _stream(dev, stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_fwd_noalloc")
+    return (o, lse) if lse is not None else o
 
 
 def attn_decode_paged_workspace_size(B, H_q, H_kv, N_q, max_blocks, block_size, d, dtype) -> int:
@@ -441,7 +480,9 @@ def attn_backward(q, k, v, o, d_o, lse, dq=None, dk=None, dv=None, *, causal: bo
     return dq, dk, dv
 
 
-__all__ = ["attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_size",
+DECODE_SCRATCH_BYTES = 64 << 20  # ATTN_DECODE_SCRATCH_BYTES in attn.h
+
+__all__ = ["attn_prefill_fwd", "attn_decode_fwd", "attn_decode_fwd_noalloc", "attn_decode_workspace_size",
            "attn_decode_paged_fwd", "attn_decode_paged_workspace_size", "attn_decode_fp8_fwd",
            "attn_decode_paged_fp8_fwd", "attn_backward", "attn_backward_workspace_size", "attn_status_string",
            "attn_version", "set_tuning", "get_tuning", "tuning", "TUNING_KNOBS", "load", "AttnError", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

@@ -90,6 +90,29 @@ void tune_init() {
 std::map<std::pair<const void*, int>, int> g_occ;
 std::mutex g_occ_mu;
 
+// ---- the no-allocation decode entry point's scratch: one array per device,
+// held for the life of the process. Host code never uses the array's name as
+// an address: the device address comes from hipGetSymbolAddress, once per
+// device with that device current, and is kept in g_scratch.
+constexpr size_t kScratchBytes = ATTN_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void* g_scratch[kMaxDevices];  // guarded by g_dev_mu
+
+int scratch_of_device(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return ATTN_ERR_LAUNCH;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return ATTN_OK;
+}
+
 size_t elem_size(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -225,7 +248,8 @@ int decode_launch(const void* q, const void* k, const void* v, size_t kv_bytes, 
                   int max_blocks, int block_size, int num_blocks, const int* kv_lens, void* o,
                   float* lse, int B, int H_q, int H_kv, int N_q, int N_kv, int d, int causal,
                   float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                  bool kv_fp8 = false, float k_scale = 1.f, float v_scale = 1.f) {
+                  bool kv_fp8 = false, float k_scale = 1.f, float v_scale = 1.f,
+                  bool use_scratch = false) {
   const bool paged = table != nullptr || block_size != 0;
   int st = check_common(B, H_q, H_kv, N_q, N_kv, d, dtype, scale);
   if (st != ATTN_OK) return st;
@@ -245,7 +269,8 @@ int decode_launch(const void* q, const void* k, const void* v, size_t kv_bytes, 
   } else if (N_kv > 0 && (k == nullptr || v == nullptr)) {
     return ATTN_ERR_NULL;
   }
-  const attn::DecodePlan plan = attn::decode_plan(B, H_q, H_kv, N_q, N_kv, d, paged);
+  const attn::DecodePlan plan =
+      attn::decode_plan(B, H_q, H_kv, N_q, N_kv, d, paged, use_scratch ? kScratchBytes : 0);
   // partial rows and work units are indexed with 32-bit integers
   const int64_t groups = ((int64_t)(H_q / H_kv) * N_q + 15) / 16;
   if ((int64_t)B * H_q * N_q * plan.splits > 0x3fffffffLL ||
@@ -254,7 +279,11 @@ int decode_launch(const void* q, const void* k, const void* v, size_t kv_bytes, 
   // contiguous caches: per-head byte offsets are 32-bit (buffer addressing)
   if (!paged && (int64_t)N_kv * d * (kv_fp8 ? 1 : elem_size(dtype)) > 0xffffffffLL)
     return ATTN_ERR_SHAPE;
-  if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE;
+  if (use_scratch) {
+    if (plan.workspace_bytes > kScratchBytes) return ATTN_ERR_WORKSPACE;
+  } else if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) {
+    return ATTN_ERR_WORKSPACE;
+  }
   const size_t es = elem_size(dtype);
   const size_t nq = (size_t)B * H_q * N_q * d * es;
   const size_t nkv = kv_bytes;
@@ -273,9 +302,13 @@ int decode_launch(const void* q, const void* k, const void* v, size_t kv_bytes, 
     return ATTN_ERR_ALIAS;
   st = check_device();
   if (st != ATTN_OK) return st;
-  float* ws = (float*)workspace;
   int dev = 0;
   (void)hipGetDevice(&dev);
+  if (use_scratch) {
+    st = scratch_of_device(dev, &workspace);
+    if (st != ATTN_OK) return st;
+  }
+  float* ws = (float*)workspace;
   // Many query rows per KV head (G * N_q, several new tokens) and enough
   // of them to fill the device: the rows are a tall product, better served by
   // the prefill kernel in rows mode (32x32 MFMA tiles, K/V shared through LDS)
@@ -323,6 +356,16 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, con
       (B > 0 && H_kv > 0 && N_kv > 0 && d > 0) ? (size_t)B * H_kv * N_kv * d * elem_size(dtype) : 0;
   return decode_launch(q, k_cache, v_cache, nkv, nullptr, 0, 0, 0, kv_lens, o, lse, B, H_q, H_kv,
                        N_q, N_kv, d, causal, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_fwd_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
+                            int N_q, int N_kv, int d, int causal, float scale, int dtype,
+                            void* stream) {
+  const size_t nkv =
+      (B > 0 && H_kv > 0 && N_kv > 0 && d > 0) ? (size_t)B * H_kv * N_kv * d * elem_size(dtype) : 0;
+  return decode_launch(q, k_cache, v_cache, nkv, nullptr, 0, 0, 0, kv_lens, o, lse, B, H_q, H_kv,
+                       N_q, N_kv, d, causal, scale, dtype, nullptr, 0, stream, false, 1.f, 1.f, true);
 }
 
 size_t attn_decode_paged_workspace_size(int B, int H_q, int H_kv, int N_q, int max_blocks,

@@ -93,7 +93,11 @@ struct DecodePlan {
   int chunk_cap;  // largest split the kernels may choose from the actual lengths
   size_t workspace_bytes;
 };
-DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool paged);
+// max_workspace > 0: if the plan's partials would exceed that many bytes, the
+// split is coarsened (contiguous caches) until they fit; a plan whose single
+// split still does not fit keeps workspace_bytes > max_workspace.
+DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool paged,
+                       size_t max_workspace = 0);
 constexpr int kDecodeMaxNq = 64;  // query tokens per request the decode path takes
 
 struct BackwardArgs {

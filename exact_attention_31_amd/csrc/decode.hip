@@ -564,7 +564,8 @@ hipError_t launch_dtype(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
-DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool paged) {
+DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool paged,
+                       size_t max_workspace) {
   // The persistent kernel hands chunks out round-robin to wavefronts. Chunks of
   // up to 2048 keys (1 MB of K and V at d = 128) keep ragged lengths balanced
   // while each wavefront's start-up latency (query and first K/V loads) stays
@@ -590,7 +591,19 @@ DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool 
   p.chunk = (int)chunk;
   p.chunk_cap = (int)cap;
   p.splits = N_kv > 0 ? (int)((N_kv + chunk - 1) / chunk) : 1;
-  p.workspace_bytes = (size_t)B * H_q * N_q * p.splits * (size_t)(d + 2) * sizeof(float);
+  const size_t per_split = (size_t)B * H_q * N_q * (size_t)(d + 2) * sizeof(float);
+  p.workspace_bytes = per_split * p.splits;
+  if (max_workspace > 0 && p.workspace_bytes > max_workspace && !paged && per_split > 0 &&
+      per_split <= max_workspace && N_kv > 0) {
+    // fewer, longer splits: the most that fit, each a multiple of the step
+    const int64_t smax = (int64_t)(max_workspace / per_split);
+    int64_t c = ((int64_t)N_kv + smax - 1) / smax;
+    c = (c + kStepKeys - 1) / kStepKeys * kStepKeys;
+    p.chunk = (int)c;
+    if (p.chunk_cap < p.chunk) p.chunk_cap = p.chunk;
+    p.splits = (int)(((int64_t)N_kv + c - 1) / c);
+    p.workspace_bytes = per_split * p.splits;
+  }
   return p;
 }
 

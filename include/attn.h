@@ -108,6 +108,30 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, con
                     void* stream);
 
 /*
+ * attn_decode_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The split partials go to a scratch array
+ * of ATTN_DECODE_SCRATCH_BYTES that the library holds on every device it runs
+ * on, for the life of the process; the call allocates and frees nothing.
+ * Arguments, layouts, results and errors are those of attn_decode_fwd, except:
+ *  - the split of the KV sequence is coarsened when the finer one's partials
+ *    (B * H_q * N_q * splits * (d + 2) * 4 bytes) would not fit the scratch,
+ *    so results can differ from attn_decode_fwd's by rounding; when even one
+ *    split does not fit (B * H_q * N_q * (d + 2) * 4 > ATTN_DECODE_SCRATCH_BYTES)
+ *    the call returns ATTN_ERR_WORKSPACE and enqueues nothing;
+ *  - every call on one device shares that device's scratch: calls that overlap
+ *    on one device (several streams, or several host threads) race and must be
+ *    ordered by the caller. No contents need clearing between calls.
+ * ATTN_ERR_LAUNCH is also returned if the scratch's device address cannot be
+ * obtained.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+int attn_decode_fwd_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int* kv_lens, void* o, float* lse, int B, int H_q, int H_kv,
+                            int N_q, int N_kv, int d, int causal, float scale, int dtype,
+                            void* stream);
+
+/*
  * Bytes of device workspace attn_decode_paged_fwd needs (0 if the sizes are
  * invalid). A pure function of its arguments.
  */

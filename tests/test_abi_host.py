@@ -209,3 +209,24 @@ def test_decode_workspace_follows_the_chunk_knob():
     with E.tuning(decode_chunk=128):
         fine = L.attn_decode_workspace_size(2, 8, 2, 1, 4096, 128, E.ATTN_BF16)
     assert fine == 2 * 8 * 1 * (4096 // 128) * 130 * 4 and fine > base
+
+
+def dfn(Nq=1, dtype=E.ATTN_BF16, lens=None, **kw):
+    a = dict(B=2, Hq=8, Hkv=1, Nkv=1000, d=128)
+    a.update(kw)
+    return L.attn_decode_fwd_noalloc(FAKE[0], FAKE[1], FAKE[2], lens, FAKE[3], None, a["B"], a["Hq"],
+                                     a["Hkv"], Nq, a["Nkv"], a["d"], 0, 0.088, dtype, None)
+
+
+def test_noalloc_decode_argument_errors_and_scratch_limit():
+    assert dfn(Nq=65) == 4 and dfn(dtype=E.ATTN_F32) == 4 and dfn(d=32) == 4
+    assert dfn(Nq=0) == 0
+    assert dfn(Hq=12, Hkv=8) == 3
+    assert dfn() == 7                 # valid: reaches the (absent) device
+    # one split of B*H_q*N_q rows of (d + 2) floats must fit the scratch
+    rows_max = E.DECODE_SCRATCH_BYTES // ((128 + 2) * 4)
+    assert dfn(B=64, Hq=(rows_max // 64) // 4 * 4, Hkv=4, Nkv=128) == 7
+    assert dfn(B=64, Hq=(rows_max // 64 + 4) // 4 * 4, Hkv=4, Nkv=128) == 5
+    # a finer split that would not fit is coarsened instead of rejected
+    assert L.attn_decode_workspace_size(64, 64, 8, 2, 2048, 128, E.ATTN_BF16) > E.DECODE_SCRATCH_BYTES
+    assert dfn(B=64, Hq=64, Hkv=8, Nq=2, Nkv=2048) == 7
