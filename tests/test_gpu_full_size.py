@@ -144,7 +144,10 @@ def test_backward_config2_full_size_sampled():
     of each gradient within 2e-2 of its largest reference entry."""
     cfg = A.CONFIGS[2]
     _announce("config 2, backward")
-    heads = [(0, 0), (1, 17), (2, 30), (3, 31)]
+    rng = np.random.default_rng(2)
+    picks = rng.choice(cfg.B * cfg.H_q, size=16, replace=False)
+    heads = sorted({(0, 0), (cfg.B - 1, cfg.H_q - 1)} | {divmod(int(x), cfg.H_q) for x in picks})
+    assert len(heads) >= 16
     q, qk = device_tensor(cfg, "q", keep=heads)
     k, kk = device_tensor(cfg, "k", keep=heads)
     v, vk = device_tensor(cfg, "v", keep=heads)
@@ -153,6 +156,7 @@ def test_backward_config2_full_size_sampled():
     dq, dk, dv = E.attn_backward(q, k, v, o, do, lse, causal=cfg.causal, scale=cfg.scale)
     torch.cuda.synchronize()
     for b, h in heads:
+        errs = []
         refs = attention_backward_ref(qk[(b, h)][None, None], kk[(b, h)][None, None],
                                       vk[(b, h)][None, None], dok[(b, h)][None, None], cfg.causal,
                                       cfg.scale)
@@ -163,4 +167,5 @@ def test_backward_config2_full_size_sampled():
             err = float(np.abs(g - r).max())
             assert np.all(np.isfinite(g)), f"{name} (b={b}, h={h}) not finite"
             assert err <= 2e-2 * mx, f"{name} (b={b}, h={h}): max|err| {err:.3e} vs max|ref| {mx:.3e}"
-        print(f"  (b={b}, h={h}) ok", flush=True)
+            errs.append(f"{name} {err:.2e} ({err / mx:.2e} of max|ref|)")
+        print(f"  (b={b}, h={h}) ok: " + ", ".join(errs), flush=True)

@@ -120,10 +120,17 @@ def test_prefill_config1_full():
     check_lse(lse.cpu().numpy().astype(np.float64), lref, 1e-4)
 
 
-def _sample_rows(N, rng, extra=48):
+def _sample_rows(N, rng, extra=48, item_rows=(128, 256)):
+    """Rows 0, 1, the last two, the middle, both sides of every boundary between
+    work items (multiples of the 128- and 256-row query blocks, where a
+    persistent workgroup hands over to its next item), tile edges near both
+    ends, and random rows."""
     base = {0, 1, N - 1, N - 2, N // 2}
     for t in (63, 64, 65, 127, 128, 129, 255, 256):
         base.update(x for x in (t, N - t) if 0 <= x < N)
+    for bm in item_rows:
+        for edge in range(bm, N, bm):
+            base.update((edge - 1, edge))
     base.update(rng.integers(0, N, size=extra).tolist())
     return np.array(sorted(base))
 
@@ -132,7 +139,8 @@ def _sample_rows(N, rng, extra=48):
 @pytest.mark.parametrize("cid", [2, 3, 4])
 def test_prefill_full_size_sampled(cid):
     """Full-size configs in the benchmark's launch configuration; every head is
-    checked on sampled rows (tile boundaries, ends, random rows)."""
+    checked on sampled rows (every work-item boundary, tile edges, ends, random
+    rows)."""
     cfg = A.CONFIGS[cid]
     _announce(f"config {cid}: {cfg.name}")
     rng = np.random.default_rng(cid)
