@@ -19,7 +19,7 @@ The default run times every workload and prints one JSON line on stdout:
   * `cpu_baseline` objects time the float64 oracle on this host's cores, on
     whole heads (or requests) of the workload for a bounded time; where only
     a sample fits, the rate is extrapolated to the whole workload and says so.
-`--only NAME` times one workload (its line's headline is that workload);
+`--only A,B` times only those workloads (the first is the line's headline);
 `--traffic-from DIR` turns rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs into
 profiles/traffic.json; `--copy-calibration` runs the copy those counters are
 calibrated against.
@@ -555,7 +555,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10, help="untimed launches first (at least)")
     ap.add_argument("--min-warmup-ms", type=float, default=200.0,
                     help="and at least this much wall time of warm-up launches per workload")
-    ap.add_argument("--only", choices=list(WORKLOADS), default=None, help="time one workload")
+    ap.add_argument("--only", default=None,
+                    help="time only these workloads (comma-separated names from: " + ", ".join(WORKLOADS) + ")")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the headline workload's CPU baseline "
@@ -587,7 +588,11 @@ def main(argv=None):
         print(json.dumps(copy_calibration(torch)), flush=True)
         return 0
 
-    names = [args.only] if args.only else DEFAULT_ORDER
+    names = [x for x in args.only.split(",") if x] if args.only else DEFAULT_ORDER
+    bad = [x for x in names if x not in WORKLOADS]
+    if bad:
+        print(f"unknown workload(s): {', '.join(bad)}", file=sys.stderr)
+        return 2
     res = {}
     cache = None
     for name in names:
