@@ -12,10 +12,11 @@ The default run times every workload and prints one JSON line on stdout:
     (B=64, H_q=32, H_kv=4, d=128, KV 32768: uniform lengths, ragged lengths,
     4 and 64 new tokens per request, a paged cache, an FP8 cache) and the
     backward of the MHA prefill;
-  * every launch is bracketed by its own pair of HIP events on the launch
-    stream: each workload reports the mean (= ms_per_step), p50, p90, min
-    and max per launch; warm-up runs at least --warmup launches and at least
-    --min-warmup-ms of GPU work (the clocks ramp during the first ~50 ms);
+  * timing uses HIP events on the launch stream: the mean (= ms_per_step)
+    over K back-to-back launches between one pair of events, then p50, p90,
+    min and max from a second pass with a pair of events around each launch;
+    warm-up runs at least --warmup launches and at least --min-warmup-ms of
+    GPU work (the clocks ramp during the first ~50 ms);
   * `cpu_baseline` objects time the float64 oracle on this host's cores, on
     whole heads (or requests) of the workload for a bounded time; where only
     a sample fits, the rate is extrapolated to the whole workload and says so.
@@ -141,9 +142,12 @@ def make_device_tensor(cfg, name, torch, threads=16):
 
 def time_launches(fn, steps, warmup, torch, min_warmup_ms=200.0):
     """Warm up (at least `warmup` calls and `min_warmup_ms` of wall time), then
-    time exactly `steps` calls, each between its own pair of HIP events on the
-    current stream (the stream the library launches on). Returns a timing dict
-    with per-launch statistics in ms."""
+    time exactly `steps` back-to-back calls between one pair of HIP events on the
+    current stream (the stream the library launches on): their mean is the step
+    time. A second pass of `steps` calls, each between its own pair of events,
+    gives the per-launch distribution (p50, p90, min, max); the events recorded
+    between launches cost a few microseconds each, so that pass is not used for
+    the mean."""
     stream = torch.cuda.current_stream()
     n_warm = 0
     t0 = time.perf_counter()
@@ -157,23 +161,31 @@ def time_launches(fn, steps, warmup, torch, min_warmup_ms=200.0):
         n_warm += 4
         torch.cuda.synchronize()
     warm_ms = (time.perf_counter() - t0) * 1e3
-    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t1 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    mean = start.elapsed_time(end) / steps
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     events[0].record(stream)
     for i in range(steps):
         fn()
         events[i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t1
     per = [events[i].elapsed_time(events[i + 1]) for i in range(steps)]
     srt = sorted(per)
 
     def pct(p):
         return srt[min(len(srt) - 1, max(0, int(math.ceil(p * len(srt))) - 1))]
 
-    return {"mean_ms": sum(per) / len(per), "p50_ms": statistics.median(per), "p90_ms": pct(0.9),
-            "min_ms": srt[0], "max_ms": srt[-1], "launches": steps, "warmup_launches": n_warm,
-            "warmup_ms": round(warm_ms, 1), "wall_s": round(wall, 3)}
+    return {"mean_ms": mean, "p50_ms": statistics.median(per), "p90_ms": pct(0.9),
+            "min_ms": srt[0], "max_ms": srt[-1], "per_launch_mean_ms": sum(per) / len(per),
+            "launches": steps, "warmup_launches": n_warm, "warmup_ms": round(warm_ms, 1),
+            "wall_s": round(wall, 3)}
 
 
 def _rate(work, ms, scale):

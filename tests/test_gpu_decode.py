@@ -211,3 +211,28 @@ def test_decode_device_chosen_split_matches_oracle(ragged):
     lens = np.random.default_rng(7).integers(1, 8193, size=40) if ragged else None
     _decode_case(40, 32, 4, 8192, 64, "bf16", lens, seed=96)
     _decode_case(40, 32, 4, 8192, 64, "bf16", lens, seed=97, Nq=3, causal=True)
+
+
+@pytest.mark.parametrize("chunk", [0, 128], ids=["plan", "fine"])
+def test_decode_workspace_contents_do_not_matter(chunk, tune):
+    """The workspace needs no initialisation: filled with NaN bytes beforehand
+    it gives the same bits as a zeroed one (ragged lengths, so most rows use
+    fewer splits than the workspace holds; 128-key splits give more than 16
+    partials per row)."""
+    if chunk:
+        tune(decode_chunk=chunk)
+    B, Hq, Hkv, N, d = 6, 16, 2, 3000, 128
+    q = to_device(A.random_tensor((B, Hq, 1, d), 601, "bf16"), "bf16")
+    k = to_device(A.random_tensor((B, Hkv, N, d), 602, "bf16"), "bf16")
+    v = to_device(A.random_tensor((B, Hkv, N, d), 603, "bf16"), "bf16")
+    lens = torch.tensor([3000, 1, 2049, 0, 700, 2999], dtype=torch.int32, device="cuda")
+    size = E.attn_decode_workspace_size(B, Hq, Hkv, 1, N, d, torch.bfloat16)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((size,), fill, dtype=torch.uint8, device="cuda")
+        o, lse = E.attn_decode_fwd(q, k, v, kv_lens=lens, workspace=ws, return_lse=True)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[1][0]).all()
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
