@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(const Split
 // of an FP8 cache, else 1). One 64-lane wavefront per query row (request,
 // query head, query index); lane i owns output column i (d = 64) or columns
 // 2i, 2i+1 (d = 128).
-template <class TT, int D, bool SPEC>
+template <class TT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part_u, const float* __restrict__ part_ml,
     const int* __restrict__ kv_lens, uint16_t* __restrict__ O, float* __restrict__ LSE,
@@ -453,77 +453,46 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);  // ((b * H_q + h) * N_q + i)
   if (bh >= BH) return;
   const int b = bh / rows_per_b;
-  const int64_t row0 = (int64_t)bh * splits;
-  // Partials in chunks of 16 splits, merged online (the running sums are
-  // rescaled when a chunk raises the maximum). The first chunk's (m, l) pairs
-  // are read before the number of splits is known (they stay within this
-  // row's partials), overlapping the reads of the lengths. With SPEC its
-  // partial outputs are read then too, up to 16 (or the plan's split count)
-  // whatever the actual count; the launch asks for that when each KV head has
-  // at most 16 query rows, where those reads are few.
-  constexpr int CH = 16;
-  float a0[CH], a1[CH];
-  auto read_u = [&](int s0, int cnt) {
-    const float* ub = part_u + (row0 + s0) * D + PER * lane;
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      if (j < cnt) {
-        if constexpr (PER == 2) {
-          const float2 v = *(const float2*)(ub + (int64_t)j * D);
-          a0[j] = v.x;
-          a1[j] = v.y;
-        } else {
-          a0[j] = ub[(int64_t)j * D];
-          a1[j] = 0.f;
-        }
-      } else {
-        a0[j] = a1[j] = 0.f;
-      }
-    }
-  };
-  auto read_ml = [&](int s0, int cnt, float& mj, float& lj) {
-    mj = kNegInf;
-    lj = 0.f;
-    if (lane < cnt) {
-      const float2 ml = *(const float2*)(part_ml + (row0 + s0 + lane) * 2);
-      mj = ml.x;
-      lj = ml.y;
-    }
-  };
-  float mj, lj;
-  const int spec = min(CH, splits);
-  read_ml(0, spec, mj, lj);
-  if constexpr (SPEC) read_u(0, spec);
   int len = kv_lens ? kv_lens[b] : N_kv;
   len = min(max(len, 0), N_kv);
   // the split kernel's units: the same function of the same inputs
   const int ce = unit_chunk(kv_lens, BH / rows_per_b, N_kv, chunk, chunk_cap, HG, nwaves);
   const int ns = (len + ce - 1) / ce;
-  float M = kNegInf, L = 0.f, U0 = 0.f, U1 = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += CH) {
-    const int cnt = min(CH, ns - s0);
-    if (s0 > 0) read_ml(s0, cnt, mj, lj);
-    if (!SPEC || s0 > 0) read_u(s0, cnt);
-    float mc = (lane < cnt) ? mj : kNegInf;
+  const int64_t row0 = (int64_t)bh * splits;
+  float M = kNegInf;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, part_ml[(row0 + s) * 2]);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mc = fmaxf(mc, __shfl_xor(mc, o));
-    const float mn = fmaxf(M, mc);
-    const float ref = (mn == kNegInf) ? 0.f : mn;
-    const float a = (M == kNegInf) ? 0.f : fast_exp2(M - ref);
-    L *= a;
-    U0 *= a;
-    U1 *= a;
-    // (partials past the last split may hold anything from earlier use of
-    // the workspace, NaN included: they are selected away, never multiplied)
-    const float w = (lane < cnt) ? fast_exp2(mj - ref) : 0.f;
-    L += (lane < cnt) ? w * lj : 0.f;
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float Mref = (M == kNegInf) ? 0.f : M;
+  float L = 0.f, U0 = 0.f, U1 = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int s = s0 + lane;
+    const float w = (s < ns) ? fast_exp2(part_ml[(row0 + s) * 2] - Mref) : 0.f;
+    L += (s < ns) ? w * part_ml[(row0 + s) * 2 + 1] : 0.f;
+    const int cnt = min(64, ns - s0);
+    const float* ub = part_u + (row0 + s0) * D + PER * lane;
+    // eight splits per batch: all loads issued before the accumulation
+    for (int j0 = 0; j0 < cnt; j0 += 8) {
+      float a0[8], a1[8];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const float wj = __shfl(w, j);
-      U0 += (j < cnt) ? wj * a0[j] : 0.f;
-      U1 += (j < cnt) ? wj * a1[j] : 0.f;
+      for (int j = 0; j < 8; ++j) {
+        const int jj = min(j0 + j, cnt - 1);
+        if constexpr (PER == 2) {
+          const float2 v = *(const float2*)(ub + (int64_t)jj * D);
+          a0[j] = v.x;
+          a1[j] = v.y;
+        } else {
+          a0[j] = ub[(int64_t)jj * D];
+          a1[j] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float wj = (j0 + j < cnt) ? __shfl(w, j0 + j) : 0.f;
+        U0 += wj * a0[j];
+        U1 += wj * a1[j];
+      }
     }
-    M = mn;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
@@ -571,7 +540,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
           : launch_kernel(decode_split_kernel<TT, D, NG, OCC, false, FP8>, grid, dim3(kThreads), st, P);
   if (e != hipSuccess) return e;
   const int BH = a.B * a.H_q * a.N_q;
-  return launch_kernel(decode_merge_kernel<TT, D, NG == 1>, dim3((BH + 3) / 4), dim3(256), st, a.part_u,
+  return launch_kernel(decode_merge_kernel<TT, D>, dim3((BH + 3) / 4), dim3(256), st, a.part_u,
                        a.part_ml, a.kv_lens, (uint16_t*)a.o, a.lse, a.H_q * a.N_q, a.N_kv, a.splits,
                        a.chunk, a.chunk_cap, a.H_kv * ngroups, (int)grid.x * 4, BH,
                        FP8 ? a.v_scale : 1.f);
