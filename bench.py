@@ -574,6 +574,7 @@ def main(argv=None):
                     help="seconds of oracle time for the headline workload's CPU baseline "
                          "(the other workloads get less)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the library GEMM reference")
+    ap.add_argument("--gemm", action="store_true", help="time the library GEMM reference with --only too")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--traffic-from", metavar="DIR", default=None,
@@ -630,7 +631,7 @@ def main(argv=None):
         res[name] = r
     del cache
     torch.cuda.empty_cache()
-    gemm = None if (args.no_gemm or args.only) else library_gemm_tflops(torch, args)
+    gemm = None if (args.no_gemm or (args.only and not args.gemm)) else library_gemm_tflops(torch, args)
 
     if not args.no_cpu:
         budgets = {"prefill_c4": args.cpu_budget, "prefill_c3": args.cpu_budget / 2,
