@@ -95,6 +95,35 @@ __device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0
 // True in every lane if `p` holds in any lane of the wavefront (uniform branch).
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
 
+// Work order of a grid with one work item per workgroup. Items are (unit,
+// block) pairs, a unit being a (batch, head) and block 0 the longest under a
+// causal mask. The hardware hands workgroup ids to the 8 XCDs round-robin and,
+// within an XCD, in increasing order, so workgroup k is the k-th item of that
+// XCD's share. Items are numbered in groups of 32 units and, within a group,
+// block-major (block 0 of each unit, then block 1, ...): every XCD gets the
+// same mix of lengths and starts with its longest blocks, the short ones
+// filling in at the end. When a group's unit count is a multiple of 8, the
+// units an XCD receives are consecutive (adjacent heads: the query heads of a
+// KV head), so what they share stays in that XCD's L2; otherwise they are
+// dealt one by one.
+struct GridItem {
+  int unit, blk;
+  bool valid;
+};
+__device__ __forceinline__ GridItem grid_item(int nblk, int nunit) {
+  constexpr int GU = 32;  // units per group (a multiple of 8)
+  const int k = blockIdx.x;
+  GridItem w;
+  w.valid = k < nblk * nunit;
+  const int g = k / (GU * nblk);
+  const int r = k - g * (GU * nblk);
+  const int gu = min(GU, nunit - g * GU);  // units in this group
+  w.blk = r / gu;
+  const int u = r - w.blk * gu;             // lands on XCD u % 8 when gu % 8 == 0
+  w.unit = g * GU + ((gu & 7) ? u : (u & 7) * (gu >> 3) + (u >> 3));
+  return w;
+}
+
 // Raw buffer resource over [base, base + nbytes): loads past the end return
 // zeros and stores past the end are dropped, with no branches in the kernel.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t nbytes) {

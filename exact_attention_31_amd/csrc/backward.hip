@@ -56,23 +56,19 @@ template <int D> struct BwdGrp {
   static __device__ __forceinline__ int row(int r) { return GRP * (r >> 2) + IN * (r & 3); }
 };
 
-// Workgroup -> (batch, head, block) with the same XCD-contiguous order as the
-// forward pass: item ranges are cut into 8 parts, XCD x takes part x, so the
-// blocks of one head run on one XCD and share its L2.
+// Workgroup -> (batch, head, block) in the work order of grid_item (block 0
+// is the longest under a causal mask in both gradient kernels).
 struct BwdItem {
   int b, h, blk;
   bool valid;
 };
 __device__ __forceinline__ BwdItem bwd_map(int nblk, int H, int B) {
-  const int id = blockIdx.x;
-  const int per_xcd = (int)gridDim.x >> 3;
-  const int item = (id & 7) * per_xcd + (id >> 3);
+  const GridItem g = grid_item(nblk, H * B);
   BwdItem w;
-  w.valid = item < nblk * H * B;
-  const int unit = item / nblk;
-  w.blk = item - unit * nblk;
-  w.b = unit / H;
-  w.h = unit - w.b * H;
+  w.valid = g.valid;
+  w.blk = g.blk;
+  w.b = g.unit / H;
+  w.h = g.unit - w.b * H;
   return w;
 }
 
@@ -410,8 +406,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   const auto rK = buffer_rsrc(K + kv_head, head_kv_bytes);
   const auto rV = buffer_rsrc(V + kv_head, head_kv_bytes);
 
-  // causal: the block with the most keys first (blocks of a head run in order on
-  // one XCD, so the short ones come last and fill in)
+  // causal: block 0 (in the work order) is the one with the most keys
   const int qblk = CAUSAL ? nqb - 1 - wi.blk : wi.blk;
   const int q0 = qblk * BM + 32 * wave;
   const int qrow = q0 + lr;

@@ -61,28 +61,20 @@ constexpr float kLazySum = 256.f;  // 2^kLazyRescale
 // workgroup). Each K or V operand read from LDS feeds QB MFMAs, so QB = 2
 // halves the LDS bytes per FLOP at the price of twice the registers (a tuning
 // alternative only: at d = 128 it spills).
-// Workgroup -> (batch, head, query block). Workgroups are handed to the 8
-// XCDs (each with its own L2) round-robin by linear id, so XCD x runs ids
-// x, x+8, x+16, ... Work items (head-major, longest query block first within a
-// head) are cut into 8 contiguous ranges and XCD x takes range x in order: the
-// query blocks of a head, and heads sharing a KV head, then run on one XCD and
-// reuse its L2, while every XCD gets the same number of items.
+// Workgroup -> (batch, head, query block), in the work order of grid_item
+// (query block 0 in that order is the one with the most keys under a causal
+// mask). The persistent grids below use their own order.
 struct WorkItem {
   int b, h, qblk;
   int valid;  // an int, not a bool: no padding bytes for a struct copy to move
 };
 __device__ __forceinline__ WorkItem map_work(int nqb, int H_q, int B, bool longest_first) {
-  const int id = blockIdx.x;
-  const int per_xcd = (int)gridDim.x >> 3;
-  const int item = (id & 7) * per_xcd + (id >> 3);
+  const GridItem g = grid_item(nqb, H_q * B);
   WorkItem w;
-  const int total = nqb * H_q * B;
-  w.valid = item < total;
-  const int unit = item / nqb;
-  const int qi = item - unit * nqb;
-  w.qblk = longest_first ? (nqb - 1 - qi) : qi;
-  w.b = unit / H_q;
-  w.h = unit - w.b * H_q;
+  w.valid = g.valid;
+  w.qblk = longest_first ? (nqb - 1 - g.blk) : g.blk;
+  w.b = g.unit / H_q;
+  w.h = g.unit - w.b * H_q;
   return w;
 }
 
@@ -122,11 +114,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
   const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
 
   // ---- work items. One per workgroup (map_work), or, persistent: the grid
-  // holds as many workgroups as can be resident, and each walks items of its
-  // XCD's contiguous range (the same ranges as map_work). Slot s of an XCD
-  // takes items s, then 2*nslots - 1 - s, then 2*nslots + s, ...: a zig-zag, so
-  // that with causal masking (items of a head ordered longest first) every
-  // slot gets a mix of long and short query blocks.
+  // holds as many workgroups as can be resident. Items, numbered head-major
+  // with the longest query block of a head first, are cut into 8 contiguous
+  // ranges, and the slots of XCD x (workgroup ids x, x+8, ...) walk range x, so
+  // a head's query blocks, and heads sharing a KV head, run on one XCD and
+  // reuse its L2. Slot s of an XCD takes items s, then 2*nslots - 1 - s, then
+  // 2*nslots + s, ...: a zig-zag, so that with causal masking every slot gets a
+  // mix of long and short query blocks.
   int round = 0;
   auto next_item = [&](WorkItem& w) -> bool {
     if constexpr (!PERSIST) {
