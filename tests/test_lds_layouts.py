@@ -84,3 +84,31 @@ def test_prefill_tile_strides_are_conflict_free(D):
     # V rows: transposing reads of 4 consecutive rows, two 16-lane groups
     # 8 dwords apart (4 rows x 16 dwords per 32 lanes)
     assert _conflict_free([(kV // 2 * i, 16) for i in range(4)])
+
+
+# the ring form's XOR swizzle, as written in prefill.hip (RingLds)
+_KSWZ = "return (r / RPB) & (CPR - 1);"
+_VSWZ = "return 4 * ((r / RPB) & (RPB == 1 ? 3 : 1));"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_ring_swizzle_is_conflict_free(D):
+    """Unpadded rows of D 16-bit elements, 16-byte chunk c of row r stored at
+    chunk c ^ swz(r): K is read 16 consecutive rows at one logical chunk per
+    LDS cycle, V by transposing reads of 4 consecutive rows x 4 chunks per 32
+    lanes. Both must hit 64 distinct banks, for every row group of a 64-key
+    tile and every chunk."""
+    src = _src("prefill.hip")
+    assert _KSWZ in src and _VSWZ in src
+    RB = 2 * D
+    CPR, RPB = D // 8, 256 // RB
+    kswz = lambda r: (r // RPB) & (CPR - 1)
+    vswz = lambda r: 4 * ((r // RPB) & (3 if RPB == 1 else 1))
+    dword = lambda r, slot: (r * RB + 16 * slot) // 4
+    for r0 in range(0, 64, 16):
+        for c in range(CPR):
+            assert _conflict_free([(dword(r, c ^ kswz(r)), 4) for r in range(r0, r0 + 16)]), (D, r0, c)
+    for r0 in range(0, 64, 4):
+        for c0 in range(0, CPR, 4):
+            acc = [(dword(r, c ^ vswz(r)), 4) for r in range(r0, r0 + 4) for c in range(c0, c0 + 4)]
+            assert _conflict_free(acc), (D, r0, c0)
