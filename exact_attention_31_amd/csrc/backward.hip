@@ -275,14 +275,14 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
         s = TT::mfma32(aq, kB[st], s);
         dp = TT::mfma32(ag, *(const u32x4_t*)(vrow + 16 * st), dp);
       }
-      // keep the Q, dO and V operand reads two k-steps ahead of their MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      // keep the Q, dO and V operand reads one k-step ahead of their MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-      for (int st = 0; st < KS - 2; ++st) {
+      for (int st = 0; st < KS - 1; ++st) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       // rows of accumulator r: query qs + 8*(r/4) + 4*lh + r%4; column: key kw + lr
       const bool need_mask = CAUSAL && (kw + 31 > qs + off);
       // element (rg, i) is query qs + 8*rg + 4*lh + i; key kw + lr is visible

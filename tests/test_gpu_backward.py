@@ -71,6 +71,11 @@ BWD = [
     (1, 4, 2, 700, 900, 64),
     (2, 2, 2, 900, 700, 64),
     (1, 2, 1, 600, 600, 64),
+    # (batch, head) unit counts around the work order's groups of 32: 33 heads
+    # (a group of 32 and one of 1), 40 (32 + 8), 7, each over several blocks
+    (1, 33, 33, 300, 300, 64),
+    (5, 8, 8, 300, 300, 128),
+    (7, 1, 1, 520, 520, 128),
 ]
 
 

@@ -53,6 +53,29 @@ def test_prefill_small_matches_oracle(shape, causal, dtype):
     _run_small(*shape, dtype, causal, seed=zlib.crc32(repr((shape, causal, dtype)).encode()) % 10000)
 
 
+# One work item per workgroup (too few items for the persistent grid): the
+# work order deals (batch, head) units in groups of 32, block-major; these unit
+# counts leave a partial group (33, 40, 70), a group that is not a multiple of
+# 8 (7, 12, 33) and one that is (32, 40's first), with several query blocks.
+ONE_ITEM_GRIDS = [
+    # B, Hq, Hkv, Nq, Nkv, d, dtype
+    (1, 33, 3, 300, 300, 64, "f16"),
+    (5, 8, 2, 520, 520, 128, "bf16"),
+    (7, 1, 1, 300, 300, 64, "bf16"),
+    (1, 12, 12, 400, 400, 64, "f16"),
+    (2, 35, 5, 260, 300, 128, "bf16"),
+    (1, 32, 4, 600, 600, 128, "f16"),
+]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("case", ONE_ITEM_GRIDS, ids=lambda c: "x".join(map(str, c)))
+def test_prefill_one_item_grid_work_order(case, causal):
+    B, Hq, Hkv, Nq, Nkv, d, dtype = case
+    _run_small(B, Hq, Hkv, Nq, Nkv, d, dtype, causal,
+               seed=zlib.crc32(repr((case, causal, "order")).encode()) % 10000)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_prefill_no_keys_gives_zero_and_neg_inf(dtype):
     q = to_device(A.random_tensor((1, 2, 5, 64), 1, dtype), dtype)

@@ -29,8 +29,6 @@ ACCEPTED = [
      "23,400-step series runs one item per workgroup, without scratch)"),
     (r"decode_split_kernelI.*Li128ELi4ELi1ELb1ELb0E", 24,
      "paged decode with four column groups per wavefront (more than 32 query rows per KV head)"),
-    (r"bwd_dkdv_kernelI.*Li128ELb1E", 12,
-     "causal dK/dV at d = 128: the two-k-step operand read-ahead holds 3 registers in scratch"),
 ]
 
 
