@@ -1,8 +1,9 @@
 """Full-size parity of the workloads that bench.py times beside the headline
 prefill: multi-token decode (4 and 64 new tokens per request), paged and FP8
 decode against config 5's 32768-token cache, and the backward pass of config
-2. Each runs in the benchmark's launch configuration on the whole batch; the
-float64 oracle then checks sampled heads one by one (MI355X only)."""
+2 (plus a GQA backward of 32 query heads over 4 KV heads). Each runs in the
+benchmark's launch configuration on the whole batch; the float64 oracle then
+checks sampled heads one by one (MI355X only)."""
 import sys
 
 import numpy as np
@@ -169,3 +170,34 @@ def test_backward_config2_full_size_sampled():
             assert err <= 2e-2 * mx, f"{name} (b={b}, h={h}): max|err| {err:.3e} vs max|ref| {mx:.3e}"
             errs.append(f"{name} {err:.2e} ({err / mx:.2e} of max|ref|)")
         print(f"  (b={b}, h={h}) ok: " + ", ".join(errs), flush=True)
+
+
+def test_backward_gqa_sampled_kv_heads():
+    """The backward of a causal GQA prefill (bf16, 32 query heads over 4 KV heads,
+    N=2048, d=128): dK and dV of a KV head sum the contributions of its 8 query
+    heads. Two KV heads are checked whole (dK, dV, and dQ of their 16 query
+    heads) against the float64 oracle; relative tolerance as for config 2."""
+    _announce("GQA backward 1x32/4x2048x128 causal")
+    B, Hq, Hkv, N, d = 1, 32, 4, 2048, 128
+    G = Hq // Hkv
+    q = A.random_tensor((B, Hq, N, d), 901, "bf16")
+    k = A.random_tensor((B, Hkv, N, d), 902, "bf16")
+    v = A.random_tensor((B, Hkv, N, d), 903, "bf16")
+    do = A.random_tensor((B, Hq, N, d), 904, "bf16")
+    scale = float(np.float32(d ** -0.5))
+    dev = [torch.from_numpy(x).cuda().to(torch.bfloat16) for x in (q, k, v, do)]
+    o, lse = E.attn_prefill_fwd(dev[0], dev[1], dev[2], causal=True, scale=scale, return_lse=True)
+    dq, dk, dv = E.attn_backward(dev[0], dev[1], dev[2], o, dev[3], lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    for g in (0, Hkv - 1):
+        hs = slice(g * G, (g + 1) * G)
+        rq, rk, rv = attention_backward_ref(q[:, hs], k[:, g:g + 1], v[:, g:g + 1], do[:, hs], True, scale)
+        errs = []
+        for name, got, ref in (("dq", dq[:, hs], rq), ("dk", dk[:, g:g + 1], rk), ("dv", dv[:, g:g + 1], rv)):
+            gh = to_host64(got)
+            mx = float(np.abs(ref).max())
+            err = float(np.abs(gh - ref).max())
+            assert np.all(np.isfinite(gh)), f"{name} (kv head {g}) not finite"
+            assert err <= 2e-2 * mx, f"{name} (kv head {g}): max|err| {err:.3e} vs max|ref| {mx:.3e}"
+            errs.append(f"{name} {err:.2e} ({err / mx:.2e} of max|ref|)")
+        print(f"  kv head {g} ok: " + ", ".join(errs), flush=True)
