@@ -86,7 +86,7 @@ DEFAULT_ORDER = ["prefill_c4", "prefill_c2", "prefill_c3", "prefill_c1", "backwa
 STEP_KERNELS = {
     "prefill": ["prefill16_kernel", "prefill16_ring_kernel", "prefill32_kernel"],
     "decode": ["decode_split_kernel", "decode_merge_kernel", "prefill16_kernel", "prefill16_ring_kernel"],
-    "backward": ["bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"],
+    "backward": ["bwd_dq_kernel", "bwd_dkdv_kernel"],
 }
 KERNEL_SOURCES = {"prefill": ["prefill.hip"], "decode": ["decode.hip", "prefill.hip"],
                   "backward": ["backward.hip"]}
@@ -275,7 +275,7 @@ def bench_backward(name, cfg, args, torch, E):
             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_MFMA_16BIT, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_MFMA_16BIT, 4), "traffic": measured_traffic(name),
                          "algorithmic_bytes": nbytes, "work_per_launch": flops,
-                         "kernel": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel (one step)"}}
+                         "kernel": "bwd_dq_kernel + bwd_dkdv_kernel (one step)"}}
 
 
 class DecodeCache:

@@ -48,6 +48,11 @@ struct BF16 {
     bf16x2_t v = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, v);
   }
+  // The low / high 16-bit value of a packed pair, exactly as a float.
+  static __device__ __forceinline__ float lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return __builtin_bit_cast(float, w & 0xffff0000u);
+  }
 };
 
 struct F16 {
@@ -62,6 +67,12 @@ struct F16 {
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     f16x2_t v = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(f16x2_t, w)[0];
+  }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(f16x2_t, w)[1];
   }
 };
 

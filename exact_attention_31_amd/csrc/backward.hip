@@ -9,15 +9,16 @@
 //   dQ = scale * dS K,   dK = scale * dS^T Q,
 // dK and dV summed over the G query heads that share a KV head.
 //
-// Three kernels, no atomics (deterministic):
-//   bwd_prep_kernel   Delta and the log-sum-exp in log2 units, per query row;
+// Two kernels, no atomics (deterministic), the dQ kernel first:
+//   bwd_dq_kernel     one workgroup per 256 query rows; each wavefront keeps
+//                     its Q and dO rows in registers, forms Delta (from its O
+//                     rows) and the log-sum-exp in log2 units for them, writes
+//                     both for the dK/dV kernel, and accumulates dQ^T while
+//                     K and V tiles stream through LDS;
 //   bwd_dkdv_kernel   one workgroup per 256 keys of a KV head; each wavefront
 //                     keeps 32 keys of K in registers (their V rows in LDS)
 //                     and accumulates dK^T, dV^T while Q and dO tiles stream
-//                     through LDS;
-//   bwd_dq_kernel     one workgroup per 256 query rows; each wavefront keeps
-//                     its Q and dO rows in registers and accumulates dQ^T while
-//                     K and V tiles stream through LDS.
+//                     through LDS.
 // Matrix-core layouts are those of the forward kernels (32x32x16 MFMA); the
 // accumulators of S (dK/dV kernel) and S^T (dQ kernel) are fed back as B
 // operands with the K-index permutation their layout implies, and the A
@@ -70,53 +71,6 @@ __device__ __forceinline__ BwdItem bwd_map(int nblk, int H, int B) {
   w.b = g.unit / H;
   w.h = g.unit - w.b * H;
   return w;
-}
-
-// Delta_i = sum_d dO_id O_id in fp32, and lse2_i = lse_i * log2(e) (+inf for a
-// row with no visible key, so that its recomputed probabilities are 0).
-// Sixteen lanes per row.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O,
-                                                       const uint16_t* __restrict__ dO,
-                                                       const float* __restrict__ LSE,
-                                                       float* __restrict__ lse2,
-                                                       float* __restrict__ delta, int64_t rows,
-                                                       bool bf16) {
-  constexpr int EPL = D / 16;  // elements per lane
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  float acc = 0.f;
-  if (row < rows) {
-    const uint16_t* o = O + row * D + sub * EPL;
-    const uint16_t* g = dO + row * D + sub * EPL;
-    uint16_t ov[EPL], gv[EPL];
-    if constexpr (EPL == 8) {
-      *(u32x4_t*)ov = *(const u32x4_t*)o;
-      *(u32x4_t*)gv = *(const u32x4_t*)g;
-    } else {
-      *(u32x2_t*)ov = *(const u32x2_t*)o;
-      *(u32x2_t*)gv = *(const u32x2_t*)g;
-    }
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      float a, c;
-      if (bf16) {
-        a = __builtin_bit_cast(float, (uint32_t)ov[i] << 16);
-        c = __builtin_bit_cast(float, (uint32_t)gv[i] << 16);
-      } else {
-        a = (float)__builtin_bit_cast(_Float16, ov[i]);
-        c = (float)__builtin_bit_cast(_Float16, gv[i]);
-      }
-      acc = __builtin_fmaf(a, c, acc);
-    }
-  }
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (row < rows && sub == 0) {
-    delta[row] = acc;
-    const float l = LSE[row];
-    lse2[row] = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -363,6 +317,11 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
 // 32*NW query rows of head h of batch b; lane: query row
 // q0 + lane % 32 as the B operand column of S^T = K Q^T and dP^T = V dO^T.
 // Key tiles of 64 rows stream through LDS (double-buffered, register-staged).
+// Before the tiles, each lane forms Delta = sum_d dO O over its half of the
+// row's d (O read in the same layout as dO) and the other half from the lane
+// 32 away, and lse2 = lse * log2(e) (+inf for a row with no visible key, so
+// that its recomputed probabilities are 0); lanes of the first half write
+// both for the dK/dV kernel, which runs after this one.
 // Per 32-key half:
 //   S^T = K Q^T, dP^T = V dO^T          (A: K, V rows from LDS; B: Q, dO in registers)
 //   P^T, dS^T per element (one lse2 and Delta per lane)
@@ -370,9 +329,9 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
 template <class TT, int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
-    uint16_t* __restrict__ dQ, int H_q, int H_kv, int N_q, int N_kv, float scale_log2, float scale,
-    int nqb, int nbatch) {
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ lse2, float* __restrict__ delta, uint16_t* __restrict__ dQ, int H_q, int H_kv,
+    int N_q, int N_kv, float scale_log2, float scale, int nqb, int nbatch) {
   constexpr int STR = BwdLds<D>::STR;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -412,14 +371,32 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   const int qrow = q0 + lr;
   const int lim = CAUSAL ? min(N_kv, max(qrow + off + 1, 0)) : N_kv;  // keys below lim visible
   u32x4_t qB[KS], gB[KS];
+  float Dl = 0.f;
+  {
+    const auto rO = buffer_rsrc(O + qh * D, head_q_bytes);
+    u32x4_t oB[KS];
 #pragma unroll
-  for (int st = 0; st < KS; ++st) {
-    qB[st] = buffer_load16(rQ, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
-    gB[st] = buffer_load16(rG, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
+    for (int st = 0; st < KS; ++st) {
+      qB[st] = buffer_load16(rQ, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
+      gB[st] = buffer_load16(rG, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
+      oB[st] = buffer_load16(rO, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
+    }
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        Dl = __builtin_fmaf(TT::lo(gB[st][w]), TT::lo(oB[st][w]), Dl);
+        Dl = __builtin_fmaf(TT::hi(gB[st][w]), TT::hi(oB[st][w]), Dl);
+      }
+    Dl += __shfl_xor(Dl, 32);
   }
   const bool in = qrow < N_q;
-  const float L2 = in ? lse2[qh + qrow] : __builtin_inff();
-  const float Dl = in ? delta[qh + qrow] : 0.f;
+  const float lse_n = in ? LSE[qh + qrow] : kNegInf;
+  const float L2 = (lse_n == kNegInf) ? __builtin_inff() : lse_n * kLog2e;
+  if (in && lh == 0) {
+    lse2[qh + qrow] = L2;
+    delta[qh + qrow] = Dl;
+  }
 
   int kv_end = N_kv;
   if (CAUSAL) {
@@ -552,16 +529,24 @@ unsigned xcd_grid(int64_t items) { return (unsigned)(((items + 7) / 8) * 8); }
 
 template <class TT, int D>
 hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
-  const int64_t rows = (int64_t)a.B * a.H_q * a.N_q;
   const float sl2 = a.scale * kLog2e;
   const auto q = (const uint16_t*)a.q;
   const auto k = (const uint16_t*)a.k;
   const auto v = (const uint16_t*)a.v;
   const auto d_o = (const uint16_t*)a.d_o;
-  if (rows > 0) {
-    const hipError_t e = launch_kernel(bwd_prep_kernel<D>, dim3((unsigned)((rows + 15) / 16)), dim3(256), st,
-                                       (const uint16_t*)a.o, d_o, a.lse, a.lse2, a.delta, rows,
-                                       a.dtype == kDtypeBF16);
+  // dQ first: it also writes lse2 and Delta for every query row
+  if (a.N_q > 0) {
+    constexpr int NW = 8;  // 256 rows per workgroup, two wavefronts per SIMD
+    const int nqb = (a.N_q + 32 * NW - 1) / (32 * NW);
+    const dim3 g(xcd_grid((int64_t)nqb * a.H_q * a.B));
+    const auto o = (const uint16_t*)a.o;
+    const hipError_t e =
+        a.causal ? launch_kernel(bwd_dq_kernel<TT, D, true, NW>, g, dim3(64 * NW), st, q, k, v, o, d_o, a.lse,
+                                 a.lse2, a.delta, (uint16_t*)a.dq, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, a.scale,
+                                 nqb, a.B)
+                 : launch_kernel(bwd_dq_kernel<TT, D, false, NW>, g, dim3(64 * NW), st, q, k, v, o, d_o, a.lse,
+                                 a.lse2, a.delta, (uint16_t*)a.dq, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, a.scale,
+                                 nqb, a.B);
     if (e != hipSuccess) return e;
   }
   if (a.N_kv > 0) {
@@ -574,19 +559,6 @@ hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
                  : launch_kernel(bwd_dkdv_kernel<TT, D, false>, g, dim3(64 * kBwdNWK), st, q, k, v, d_o,
                                  a.lse2, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H_q, a.H_kv, a.N_q,
                                  a.N_kv, sl2, a.scale, nkb, a.B);
-    if (e != hipSuccess) return e;
-  }
-  if (a.N_q > 0) {
-    constexpr int NW = 8;  // 256 rows per workgroup, two wavefronts per SIMD
-    const int nqb = (a.N_q + 32 * NW - 1) / (32 * NW);
-    const dim3 g(xcd_grid((int64_t)nqb * a.H_q * a.B));
-    const hipError_t e =
-        a.causal ? launch_kernel(bwd_dq_kernel<TT, D, true, NW>, g, dim3(64 * NW), st, q, k, v, d_o, a.lse2,
-                                 a.delta, (uint16_t*)a.dq, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, a.scale, nqb,
-                                 a.B)
-                 : launch_kernel(bwd_dq_kernel<TT, D, false, NW>, g, dim3(64 * NW), st, q, k, v, d_o, a.lse2,
-                                 a.delta, (uint16_t*)a.dq, a.H_q, a.H_kv, a.N_q, a.N_kv, sl2, a.scale, nqb,
-                                 a.B);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -221,10 +221,10 @@ size_t attn_backward_workspace_size(int B, int H_q, int H_kv, int N_q, int N_kv,
  *   causal, scale: as for attn_prefill_fwd (bottom-right alignment);
  *   workspace: attn_backward_workspace_size(...) bytes, overwritten.
  * dq, dk, dv are written in full (no accumulation into them); they must not
- * overlap any input, each other or the workspace. Three kernels run on
- * `stream`: per-row Delta, then dK/dV (one workgroup per 256 keys), then dQ
- * (one workgroup per 256 query rows); no atomics, so results are
- * deterministic.
+ * overlap any input, each other or the workspace. Two kernels run on
+ * `stream`: dQ (one workgroup per 256 query rows), which also leaves each
+ * row's Delta and log2-unit LSE in the workspace, then dK/dV (one workgroup
+ * per 256 keys); no atomics, so results are deterministic.
  * Work: 10*d FLOP per visible (query, key) pair per query head in the five
  * products (the recomputation adds 4*d more).
  */

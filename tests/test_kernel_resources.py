@@ -40,7 +40,7 @@ def test_report_matches_the_sources():
 def test_kernels_are_in_the_report():
     names = " ".join(REPORT["kernels"])
     for k in ("prefill16_kernel", "prefill16_ring_kernel", "prefill32_kernel", "decode_split_kernel",
-              "decode_merge_kernel", "bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"):
+              "decode_merge_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"):
         assert k in names, k
 
 
@@ -61,10 +61,10 @@ def test_default_forms_do_not_spill():
     """The kernels the benchmarked workloads run: the persistent d = 128
     prefill (staged form), the one-item-per-workgroup d = 64 ring form, the
     decode split and merge kernels with one or two column groups, and the
-    backward's prep and dQ kernels."""
+    backward's dQ and dK/dV kernels."""
     pats = [r"prefill16_kernelI.*Li128ELb1ELi1ELi8ELb1E", r"prefill16_ring_kernelI.*Li64ELb1ELi4ELb0E",
             r"decode_split_kernelI.*Li128ELi1ELi2ELb0ELb0E", r"decode_split_kernelI.*Li128ELi1ELi2ELb0ELb1E",
-            r"decode_merge_kernel", r"bwd_prep_kernel", r"bwd_dq_kernelI.*Li128ELb1E"]
+            r"decode_merge_kernel", r"bwd_dq_kernelI.*Li128ELb1E", r"bwd_dkdv_kernelI.*Li128ELb1E"]
     for pat in pats:
         hits = [n for n in REPORT["kernels"] if re.search(pat, n)]
         assert hits, pat
