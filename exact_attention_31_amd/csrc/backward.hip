@@ -370,33 +370,16 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   const int q0 = qblk * BM + 32 * wave;
   const int qrow = q0 + lr;
   const int lim = CAUSAL ? min(N_kv, max(qrow + off + 1, 0)) : N_kv;  // keys below lim visible
-  u32x4_t qB[KS], gB[KS];
-  float Dl = 0.f;
-  {
-    const auto rO = buffer_rsrc(O + qh * D, head_q_bytes);
-    u32x4_t oB[KS];
+  u32x4_t qB[KS], gB[KS], oB[KS];
+  const auto rO = buffer_rsrc(O + qh * D, head_q_bytes);
 #pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      qB[st] = buffer_load16(rQ, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
-      gB[st] = buffer_load16(rG, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
-      oB[st] = buffer_load16(rO, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
-    }
-#pragma unroll
-    for (int st = 0; st < KS; ++st)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        Dl = __builtin_fmaf(TT::lo(gB[st][w]), TT::lo(oB[st][w]), Dl);
-        Dl = __builtin_fmaf(TT::hi(gB[st][w]), TT::hi(oB[st][w]), Dl);
-      }
-    Dl += __shfl_xor(Dl, 32);
+  for (int st = 0; st < KS; ++st) {
+    qB[st] = buffer_load16(rQ, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
+    gB[st] = buffer_load16(rG, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
+    oB[st] = buffer_load16(rO, (uint32_t)(qrow * D + 16 * st + 8 * lh) * 2);
   }
   const bool in = qrow < N_q;
   const float lse_n = in ? LSE[qh + qrow] : kNegInf;
-  const float L2 = (lse_n == kNegInf) ? __builtin_inff() : lse_n * kLog2e;
-  if (in && lh == 0) {
-    lse2[qh + qrow] = L2;
-    delta[qh + qrow] = Dl;
-  }
 
   int kv_end = N_kv;
   if (CAUSAL) {
@@ -439,10 +422,23 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   const int t_lane = Gp::row(4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) + 16 * ((lane >> 4) & 1) +
                      4 * (lane & 3);
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  if (ntiles > 0) load_tile(0);
+  // ---- this row's Delta and lse2 (O and dO arrive while tile 0 is loading)
+  float Dl = 0.f;
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      Dl = __builtin_fmaf(TT::lo(gB[st][w]), TT::lo(oB[st][w]), Dl);
+      Dl = __builtin_fmaf(TT::hi(gB[st][w]), TT::hi(oB[st][w]), Dl);
+    }
+  Dl += __shfl_xor(Dl, 32);
+  const float L2 = (lse_n == kNegInf) ? __builtin_inff() : lse_n * kLog2e;
+  if (in && lh == 0) {
+    lse2[qh + qrow] = L2;
+    delta[qh + qrow] = Dl;
   }
+  if (ntiles > 0) store_tile(0);
   vmem_wait_all();
   __syncthreads();
 
