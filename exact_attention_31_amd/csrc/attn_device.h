@@ -78,8 +78,12 @@ struct F16 {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// max of three (one v_max3_f32)
-__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+// Maxima that propagate NaN (v_maximum3_f32 / v_maximum_f32). Unlike fmaxf
+// they need no quieting of their inputs, which costs an extra instruction per
+// operand that the compiler cannot prove canonical (MFMA results, lane
+// exchanges).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 
 // Exchange with the lane 32 positions away (the other half of the wavefront).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
@@ -89,7 +93,7 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 __device__ __forceinline__ float half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
                                                   __builtin_bit_cast(uint32_t, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  return vmax(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 __device__ __forceinline__ float half_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),

@@ -112,6 +112,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
   const int lr = lane & 31;
   const int lh = lane >> 5;
   const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
+  const float inv_scale_log2 = 1.f / scale_log2;
 
   // ---- work items. One per workgroup (map_work), or, persistent: the grid
   // holds as many workgroups as can be resident. Items, numbered head-major
@@ -258,13 +259,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
     const Ctx cn = ctx_of(nwi);
 
     f32x16_t oacc[QB][DB];
-    float m[QB], l[QB];
+    float m[QB], l[QB], nm[QB], thr[QB];
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
 #pragma unroll
       for (int i = 0; i < DB; ++i) oacc[j][i] = f32x16_t{0};
       m[j] = kNegInf;  // reference maximum, in units of log2 (scores * scale * log2 e)
       l[j] = 0.f;      // this half-wave's part of the denominator
+      nm[j] = 0.f;     // the exponent offset: -m, or 0 while m is -inf
+      thr[j] = kNegInf;  // m + kLazyRescale in raw score units (scale > 0)
     }
     const int ntiles = c.ntiles;
 
@@ -330,31 +333,33 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
         uint32_t pk[QB][16];
 #pragma unroll
         for (int j = 0; j < QB; ++j) {
-          // ---- row max of the raw scores (scale > 0 commutes with max)
-          float mx = max3(s[j][0][0], s[j][0][1], s[j][1][0]);
+          // ---- row max of the raw scores (scale > 0 commutes with max), compared
+          // with the rescale threshold in the same raw units
+          float mx = vmax(s[j][0][0], s[j][1][0]);
 #pragma unroll
           for (int r = 1; r < 16; ++r) mx = max3(mx, s[j][0][r], s[j][1][r]);
-          mx = fmaxf(mx, s[j][1][0]);
-          const float mxs = half_max(mx) * scale_log2;
+          const float hm = half_max(mx);
           // The branch is wavefront-uniform, but each lane moves only its own
           // reference (alpha = 1 is an exact multiply), so a row's arithmetic never
           // depends on the other rows of the wavefront.
-          const bool need = mxs > m[j] + kLazyRescale;
+          const bool need = hm > thr[j];
           if (wave_any(need)) {
+            const float mxs = hm * scale_log2;
             const float alpha = need ? ((m[j] == kNegInf) ? 0.f : fast_exp2(m[j] - mxs)) : 1.f;
             m[j] = need ? mxs : m[j];
+            nm[j] = (m[j] == kNegInf) ? 0.f : -m[j];
+            thr[j] = (m[j] + kLazyRescale) * inv_scale_log2;
             l[j] *= alpha;
 #pragma unroll
             for (int i = 0; i < DB; ++i) oacc[j][i] *= alpha;
           }
-          const float nm = (m[j] == kNegInf) ? 0.f : -m[j];
           // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(__builtin_fmaf(s[j][0][r], scale_log2, nm));
-            const float p1 = fast_exp2(__builtin_fmaf(s[j][0][r + 1], scale_log2, nm));
-            const float p2 = fast_exp2(__builtin_fmaf(s[j][1][r], scale_log2, nm));
-            const float p3 = fast_exp2(__builtin_fmaf(s[j][1][r + 1], scale_log2, nm));
+            const float p0 = fast_exp2(__builtin_fmaf(s[j][0][r], scale_log2, nm[j]));
+            const float p1 = fast_exp2(__builtin_fmaf(s[j][0][r + 1], scale_log2, nm[j]));
+            const float p2 = fast_exp2(__builtin_fmaf(s[j][1][r], scale_log2, nm[j]));
+            const float p3 = fast_exp2(__builtin_fmaf(s[j][1][r + 1], scale_log2, nm[j]));
             l[j] += (p0 + p1) + (p2 + p3);
             pk[j][r >> 1] = TT::pack2(p0, p1);
             pk[j][8 + (r >> 1)] = TT::pack2(p2, p3);
@@ -731,10 +736,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<1, D>::kWaves)) void pr
         }
         if (slow) {
           // ---- row max of the raw scores (scale > 0 commutes with max)
-          float mx = max3(s0[0], s0[1], s1[0]);
+          float mx = vmax(s0[0], s1[0]);
 #pragma unroll
           for (int r = 1; r < 16; ++r) mx = max3(mx, s0[r], s1[r]);
-          mx = fmaxf(mx, s1[0]);
           const float mxs = half_max(mx) * scale_log2;
           // wavefront-uniform branch; each lane moves only its own reference
           // (after a failed fast path, to the tile's maximum whenever it is higher)
