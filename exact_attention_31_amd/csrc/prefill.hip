@@ -57,6 +57,65 @@ template <int D> struct Lds16 {
 constexpr float kLazyRescale = 8.f;
 constexpr float kLazySum = 256.f;  // 2^kLazyRescale
 
+// One 64-key tile of the online softmax for one lane's row (32 of its 64
+// scores in s0, s1; lane i + 32 holds the other 32): P = exp2(S * scale*log2e
+// - m), rounded to 16 bits as the PV operand, and l and the output
+// accumulators rescaled when the reference moves. The exponentials are first
+// taken against the current reference m, without the tile's row maximum: if
+// both halves of the row sum to at most 2^kLazyRescale, each is at most that,
+// which is all the lazy rescale rule asks, and they stand. Otherwise (and
+// while m is still -inf) the row raises m to the tile's maximum if that is
+// higher, rescales, and takes them again. The second pass is a
+// wavefront-uniform branch, but a row whose first pass stood keeps its
+// reference and recomputes the same values in the same order, so a row's
+// result never depends on the other rows of the wavefront.
+template <class TT, int DB>
+__device__ __forceinline__ void softmax_tile(const f32x16_t& s0, const f32x16_t& s1, float scale_log2,
+                                             float& m, float& nm, float& l, f32x16_t (&oacc)[DB],
+                                             uint32_t (&pk)[16]) {
+  auto exps = [&]() {
+    float ts = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = fast_exp2(__builtin_fmaf(s0[r], scale_log2, nm));
+      const float p1 = fast_exp2(__builtin_fmaf(s0[r + 1], scale_log2, nm));
+      const float p2 = fast_exp2(__builtin_fmaf(s1[r], scale_log2, nm));
+      const float p3 = fast_exp2(__builtin_fmaf(s1[r + 1], scale_log2, nm));
+      ts += (p0 + p1) + (p2 + p3);
+      pk[r >> 1] = TT::pack2(p0, p1);
+      pk[8 + (r >> 1)] = TT::pack2(p2, p3);
+    }
+    return ts;
+  };
+  float ts = exps();
+  // A lane fails when its 32 sum to more than 2^kLazyRescale (inf and NaN
+  // included) or m is still -inf. Lanes i and i + 32 hold the same row and
+  // reference and must take the same decision: a row fails if either fails
+  // (the exchange is on the scalar ballot mask).
+  const bool lane_fail = !(ts <= kLazySum) || m == kNegInf;
+  if (wave_any(lane_fail)) {
+    const uint64_t fail = __ballot(lane_fail);
+    const uint64_t row_fail = fail | (fail >> 32) | (fail << 32);
+    const bool ok = ((row_fail >> __lane_id()) & 1) == 0;
+    // ---- row max of the raw scores (scale > 0 commutes with max)
+    float mx = vmax(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = max3(mx, s0[r], s1[r]);
+    const float mxs = half_max(mx) * scale_log2;
+    const bool need = !ok && mxs > m;
+    if (wave_any(need)) {
+      const float alpha = need ? ((m == kNegInf) ? 0.f : fast_exp2(m - mxs)) : 1.f;
+      m = need ? mxs : m;
+      nm = (m == kNegInf) ? 0.f : -m;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+    }
+    ts = exps();
+  }
+  l += ts;
+}
+
 // QB query blocks of 32 rows per wavefront (NW * 32 * QB rows per
 // workgroup). Each K or V operand read from LDS feeds QB MFMAs, so QB = 2
 // halves the LDS bytes per FLOP at the price of twice the registers (a tuning
@@ -112,7 +171,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
   const int lr = lane & 31;
   const int lh = lane >> 5;
   const uint32_t head_q_bytes = (uint32_t)N_q * D * 2;
-  const float inv_scale_log2 = 1.f / scale_log2;
 
   // ---- work items. One per workgroup (map_work), or, persistent: the grid
   // holds as many workgroups as can be resident. Items, numbered head-major
@@ -259,7 +317,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
     const Ctx cn = ctx_of(nwi);
 
     f32x16_t oacc[QB][DB];
-    float m[QB], l[QB], nm[QB], thr[QB];
+    float m[QB], l[QB], nm[QB];
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
 #pragma unroll
@@ -267,7 +325,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
       m[j] = kNegInf;  // reference maximum, in units of log2 (scores * scale * log2 e)
       l[j] = 0.f;      // this half-wave's part of the denominator
       nm[j] = 0.f;     // the exponent offset: -m, or 0 while m is -inf
-      thr[j] = kNegInf;  // m + kLazyRescale in raw score units (scale > 0)
     }
     const int ntiles = c.ntiles;
 
@@ -304,17 +361,22 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4 * QB, 0);
-        // V^T operands of this tile, requested now so that the score MFMAs, the
-        // row max and the exponentials cover their LDS latency
+        // V^T operands of the first VE 16-key steps, requested now so that the
+        // score MFMAs and the exponentials cover their LDS latency; the rest after
+        // the exponentials (fewer registers live across them), covered by the
+        // products of the first steps.
+        constexpr int VE = (QB == 2) ? 4 : (NW == 8 && D == 128) ? 3 : 2;
         u32x4_t vop[4][DB];
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4)
+        auto read_v = [&](int t4) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             const u32x2_t lo = lds_read_tr16(tV + 16 * t4 * VST + db * 32);
             const u32x2_t hi = lds_read_tr16(tV + (16 * t4 + 8) * VST + db * 32);
             vop[t4][db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
           }
+        };
+#pragma unroll
+        for (int t4 = 0; t4 < VE; ++t4) read_v(t4);
         // ---- mask (tail and causal diagonal tiles only), branch-free per element
         const bool need_mask = kv0 + kBN > c.lo_lim;
         if (need_mask) {
@@ -330,40 +392,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<QB, D>::kWaves)) void p
             }
           }
         }
+        // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
         uint32_t pk[QB][16];
 #pragma unroll
-        for (int j = 0; j < QB; ++j) {
-          // ---- row max of the raw scores (scale > 0 commutes with max), compared
-          // with the rescale threshold in the same raw units
-          float mx = vmax(s[j][0][0], s[j][1][0]);
+        for (int j = 0; j < QB; ++j)
+          softmax_tile<TT, DB>(s[j][0], s[j][1], scale_log2, m[j], nm[j], l[j], oacc[j], pk[j]);
+        if constexpr (VE < 4) {
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int r = 1; r < 16; ++r) mx = max3(mx, s[j][0][r], s[j][1][r]);
-          const float hm = half_max(mx);
-          // The branch is wavefront-uniform, but each lane moves only its own
-          // reference (alpha = 1 is an exact multiply), so a row's arithmetic never
-          // depends on the other rows of the wavefront.
-          const bool need = hm > thr[j];
-          if (wave_any(need)) {
-            const float mxs = hm * scale_log2;
-            const float alpha = need ? ((m[j] == kNegInf) ? 0.f : fast_exp2(m[j] - mxs)) : 1.f;
-            m[j] = need ? mxs : m[j];
-            nm[j] = (m[j] == kNegInf) ? 0.f : -m[j];
-            thr[j] = (m[j] + kLazyRescale) * inv_scale_log2;
-            l[j] *= alpha;
-#pragma unroll
-            for (int i = 0; i < DB; ++i) oacc[j][i] *= alpha;
-          }
-          // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(__builtin_fmaf(s[j][0][r], scale_log2, nm[j]));
-            const float p1 = fast_exp2(__builtin_fmaf(s[j][0][r + 1], scale_log2, nm[j]));
-            const float p2 = fast_exp2(__builtin_fmaf(s[j][1][r], scale_log2, nm[j]));
-            const float p3 = fast_exp2(__builtin_fmaf(s[j][1][r + 1], scale_log2, nm[j]));
-            l[j] += (p0 + p1) + (p2 + p3);
-            pk[j][r >> 1] = TT::pack2(p0, p1);
-            pk[j][8 + (r >> 1)] = TT::pack2(p2, p3);
-          }
+          for (int t4 = VE; t4 < 4; ++t4) read_v(t4);
         }
         // ---- O^T += V^T P^T, four 16-key steps; V^T through the transposing LDS read,
         // each V operand feeding QB MFMAs
@@ -649,6 +686,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<1, D>::kWaves)) void pr
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[i] = f32x16_t{0};
     float m = kNegInf;  // reference maximum, in units of log2 (scores * scale * log2 e)
+    float nm = 0.f;     // the exponent offset: -m, or 0 while m is -inf
     float l = 0.f;      // this half-wave's part of the denominator
     const int ntiles = c.ntiles;
 
@@ -702,67 +740,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<1, D>::kWaves)) void pr
             s1[r] = (e + 32 < rel) ? s1[r] : kNegInf;
           }
         }
+        // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
         uint32_t pk[16];
-        // ---- fast path (d = 64, where the vector ALUs bound the loop): the
-        // exponentials against the current reference m, without the tile's row
-        // maximum. If this lane's 32 of them sum to at most 2^kLazyRescale, each
-        // is at most that, which is all the lazy rescale rule asks. Otherwise
-        // (or while m is still -inf) the full rule below runs on the same
-        // scores, raising m to the tile's maximum.
-        bool slow = true;
-        bool raise_all = false;
-        if constexpr (D == 64) {
-          slow = wave_any(m == kNegInf);
-          if (!slow) {
-            const float nmf = -m;
-            float ts = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-              const float p0 = fast_exp2(__builtin_fmaf(s0[r], scale_log2, nmf));
-              const float p1 = fast_exp2(__builtin_fmaf(s0[r + 1], scale_log2, nmf));
-              const float p2 = fast_exp2(__builtin_fmaf(s1[r], scale_log2, nmf));
-              const float p3 = fast_exp2(__builtin_fmaf(s1[r + 1], scale_log2, nmf));
-              ts += (p0 + p1) + (p2 + p3);
-              pk[r >> 1] = TT::pack2(p0, p1);
-              pk[8 + (r >> 1)] = TT::pack2(p2, p3);
-            }
-            if (wave_any(!(ts <= kLazySum))) {  // (also catches inf and NaN)
-              slow = true;
-              raise_all = true;
-            } else {
-              l += ts;
-            }
-          }
-        }
-        if (slow) {
-          // ---- row max of the raw scores (scale > 0 commutes with max)
-          float mx = vmax(s0[0], s1[0]);
-#pragma unroll
-          for (int r = 1; r < 16; ++r) mx = max3(mx, s0[r], s1[r]);
-          const float mxs = half_max(mx) * scale_log2;
-          // wavefront-uniform branch; each lane moves only its own reference
-          // (after a failed fast path, to the tile's maximum whenever it is higher)
-          const bool need = raise_all ? (mxs > m) : (mxs > m + kLazyRescale);
-          if (wave_any(need)) {
-            const float alpha = need ? ((m == kNegInf) ? 0.f : fast_exp2(m - mxs)) : 1.f;
-            m = need ? mxs : m;
-            l *= alpha;
-#pragma unroll
-            for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-          }
-          const float nm = (m == kNegInf) ? 0.f : -m;
-          // ---- P = exp2(S * scale*log2e - m), packed to 16-bit as the B operand
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(__builtin_fmaf(s0[r], scale_log2, nm));
-            const float p1 = fast_exp2(__builtin_fmaf(s0[r + 1], scale_log2, nm));
-            const float p2 = fast_exp2(__builtin_fmaf(s1[r], scale_log2, nm));
-            const float p3 = fast_exp2(__builtin_fmaf(s1[r + 1], scale_log2, nm));
-            l += (p0 + p1) + (p2 + p3);
-            pk[r >> 1] = TT::pack2(p0, p1);
-            pk[8 + (r >> 1)] = TT::pack2(p2, p3);
-          }
-        }
+        softmax_tile<TT, DB>(s0, s1, scale_log2, m, nm, l, oacc, pk);
         // ---- O^T += V^T P^T, four 16-key steps
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {

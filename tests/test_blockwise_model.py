@@ -17,14 +17,14 @@ def _vis(Nq, n, causal):
 
 
 @pytest.mark.parametrize("block", [1, 3, 16, 64, 1000])
-@pytest.mark.parametrize("lazy", [0.0, 8 * np.log(2)])
+@pytest.mark.parametrize("lazy,lazy_sum", [(0.0, None), (8 * np.log(2), None), (0.0, 256.0)])
 @pytest.mark.parametrize("causal,Nq,n", [(False, 37, 53), (True, 50, 50), (True, 20, 45), (True, 30, 10)])
-def test_blockwise_equals_definition(block, lazy, causal, Nq, n):
+def test_blockwise_equals_definition(block, lazy, lazy_sum, causal, Nq, n):
     d = 16
     q = rng.standard_normal((Nq, d)) * 2
     k = rng.standard_normal((n, d)) * 2
     v = rng.standard_normal((n, d))
-    o, m, l = online_rows(q, k, v, 0.25, _vis(Nq, n, causal), block, lazy)
+    o, m, l = online_rows(q, k, v, 0.25, _vis(Nq, n, causal), block, lazy, lazy_sum)
     oref, lref = attention_ref(q[None, None], k[None, None], v[None, None], causal, 0.25)
     np.testing.assert_allclose(o, oref[0, 0], atol=1e-12)
     with np.errstate(divide="ignore"):
