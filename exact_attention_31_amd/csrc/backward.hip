@@ -82,7 +82,8 @@ __device__ __forceinline__ BwdItem bwd_map(int nblk, int H, int B) {
 // wavefronts per SIMD. Query tiles of 64 rows of each of the G query heads
 // stream through LDS (double-buffered, register-staged). Per 32-row subtile:
 //   S  = Q K^T, dP = dO V^T           (A: Q, dO rows from LDS; B: K in registers, V from LDS)
-//   P  = exp2(S * scale*log2e - lse2), dS = P o (dP - Delta)   (per element)
+//   P  = exp2(S * scale*log2e - lse2), dS = P o (dP - Delta)   (per element;
+//                                      dP's accumulator starts from -Delta)
 //   dV^T += dO^T P,  dK^T += Q^T dS   (A: dO^T, Q^T by transposing LDS reads;
 //                                      B: P, dS straight from the accumulators)
 template <class TT, int D, bool CAUSAL>
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
       const int r = q0 + (tid & (kBwdBM - 1));
       const bool in = r < N_q;
       if (tid < kBwdBM) lbuf = in ? lse2[qh + r] : __builtin_inff();
-      else lbuf = in ? delta[qh + r] : 0.f;
+      else lbuf = in ? -delta[qh + r] : 0.f;
     }
   };
   auto store_tile = [&](int buf) {
@@ -221,7 +222,15 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
       if (CAUSAL && qs + 31 + off < kw) continue;
       const uint16_t* tq = &sQ[buf][0] + 8 * Gp::GRP * sub;  // row 32*sub
       const uint16_t* tg = &sG[buf][0] + 8 * Gp::GRP * sub;
-      f32x16_t s = f32x16_t{0}, dp = f32x16_t{0};
+      // dP - Delta in one go: the accumulator of dP starts from -Delta of each
+      // element's query (LDS holds -Delta in the accumulator's row order)
+      f32x16_t s = f32x16_t{0}, dp;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4_t D4 = *(const f32x4_t*)(&sD[buf][32 * sub + 8 * rg + 4 * lh]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dp[4 * rg + i] = D4[i];
+      }
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
         const u32x4_t aq = *(const u32x4_t*)(tq + a_lane + 16 * st);
@@ -230,7 +239,8 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
         dp = TT::mfma32(ag, *(const u32x4_t*)(vrow + 16 * st), dp);
       }
       // keep the Q, dO and V operand reads one k-step ahead of their MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      // (the -Delta reads first)
+      __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);
 #pragma unroll
       for (int st = 0; st < KS - 1; ++st) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -249,7 +259,6 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const f32x4_t L4 = *(const f32x4_t*)(&sL[buf][32 * sub + 8 * rg + 4 * lh]);
-          const f32x4_t D4 = *(const f32x4_t*)(&sD[buf][32 * sub + 8 * rg + 4 * lh]);
           float p[4], ds[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
             float pv = fast_exp2(__builtin_fmaf(s[r], scale_log2, -L4[i]));
             if (masked) pv = (8 * rg + i >= thr) ? pv : 0.f;
             p[i] = pv;
-            ds[i] = pv * (dp[r] - D4[i]);
+            ds[i] = pv * dp[r];
           }
           pp[2 * rg] = TT::pack2(p[0], p[1]);
           pp[2 * rg + 1] = TT::pack2(p[2], p[3]);
@@ -324,7 +333,8 @@ __global__ __launch_bounds__(64 * kBwdNWK, 2) void bwd_dkdv_kernel(
 // both for the dK/dV kernel, which runs after this one.
 // Per 32-key half:
 //   S^T = K Q^T, dP^T = V dO^T          (A: K, V rows from LDS; B: Q, dO in registers)
-//   P^T, dS^T per element (one lse2 and Delta per lane)
+//   P^T, dS^T per element (one lse2 and Delta per lane; dP^T's accumulator
+//                                        starts from -Delta)
 //   dQ^T += K^T dS^T                     (A: K^T by transposing LDS reads; B: dS^T)
 template <class TT, int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
@@ -441,6 +451,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   if (ntiles > 0) store_tile(0);
   vmem_wait_all();
   __syncthreads();
+  const f32x16_t negD = f32x16_t(-Dl);
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
@@ -453,7 +464,9 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
       if (CAUSAL && ks > q0 + 31 + off) continue;
       const uint16_t* tk = &sK[buf][0] + 8 * Gp::GRP * kb;  // row 32*kb
       const uint16_t* tv = &sV[buf][0] + 32 * kb * STR;
-      f32x16_t s = f32x16_t{0}, dp = f32x16_t{0};
+      // dP - Delta in one go: the accumulator of dP^T starts from -Delta (every
+      // element of a lane belongs to the lane's query row)
+      f32x16_t s = f32x16_t{0}, dp = negD;
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
         const u32x4_t ak = *(const u32x4_t*)(tk + ak_lane + 16 * st);
@@ -486,7 +499,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
             p0 = e < thr ? p0 : 0.f;
             p1 = e + 1 < thr ? p1 : 0.f;
           }
-          pd[r >> 1] = TT::pack2(p0 * (dp[r] - Dl), p1 * (dp[r + 1] - Dl));
+          pd[r >> 1] = TT::pack2(p0 * dp[r], p1 * dp[r + 1]);
         }
       };
       if (need_mask)
