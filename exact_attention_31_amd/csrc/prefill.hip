@@ -51,9 +51,10 @@ template <int D> struct Lds16 {
 };
 
 // Rescale threshold (log2 units): a row's reference maximum is only raised when
-// a block's maximum exceeds it by more than this, so most blocks skip the
-// rescale of l and u. Probabilities then stay below 2^8, and l and u keep one
-// common reference point, so u / l is unchanged.
+// a block's probabilities against it could exceed 2^kLazyRescale (see
+// softmax_tile), so most blocks skip the rescale of l and u. Probabilities then
+// stay below 2^8, and l and u keep one common reference point, so u / l is
+// unchanged.
 constexpr float kLazyRescale = 8.f;
 constexpr float kLazySum = 256.f;  // 2^kLazyRescale
 
@@ -716,8 +717,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : Occ<1, D>::kWaves)) void pr
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        // V^T operands of this tile, requested now so that the score MFMAs, the
-        // row max and the exponentials cover their LDS latency
+        // V^T operands of this tile, requested now so that the score MFMAs and
+        // the exponentials cover their LDS latency
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
