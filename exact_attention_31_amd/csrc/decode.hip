@@ -67,24 +67,24 @@ struct SplitParams {
   const int* kv_lens;
   float* part_u;
   float* part_ml;
-  int B, H_q, H_kv, N_q, N_kv, causal, splits, chunk, chunk_cap;
+  int B, H_q, H_kv, N_q, N_kv, causal, chunk, chunk_cap;
   float scale_log2;  // softmax scale * log2(e) (times the K dequantisation scale for FP8)
 };
 
 // Keys per work unit, chosen on the device from the requests' actual lengths.
 // The host plan's chunk sizes the workspace (ceil(N_kv / chunk) partials per
-// query row); a larger chunk never needs more. When every request has the
-// same length, the split grows from the batch's keys per wavefront (up to
-// cap) until the units of the whole batch number at most one per wavefront of
-// the grid: every wavefront still gets a unit, and the per-unit costs
-// (start-up, the partial results and their merge) are paid as few times as
-// possible. Unequal lengths keep the plan's finer split, which balances them
-// better. Each lane reads the lengths of requests lane, lane + 64, ... at
-// once, and the sums are wavefront reductions; the unit counts use a float
-// reciprocal (a heuristic needs no exact division). The result is a pure
-// function of the arguments: the merge kernel evaluates it on the same inputs
-// as the split kernel. Above kAdaptMaxB requests the plan's chunk is kept.
-// Called by all 64 lanes of a wavefront.
+// query row); a larger chunk never needs more. The split grows from the
+// batch's keys per wavefront (at least the plan's chunk, at most cap) until
+// the units of the whole batch number at most one per wavefront of the grid:
+// every wavefront still gets a unit (short requests in a long cache spread
+// over the whole grid), no wavefront gets two (which would double its time),
+// and the per-unit costs (start-up, the partial results and their merge) are
+// paid as few times as possible. Each lane reads the lengths of requests
+// lane, lane + 64, ... at once, and the sums are wavefront reductions; the
+// unit counts use a float reciprocal (a heuristic needs no exact division).
+// The result is a pure function of the arguments: the merge kernel evaluates
+// it on the same inputs as the split kernel. Above kAdaptMaxB requests the
+// plan's chunk is kept. Called by all 64 lanes of a wavefront.
 constexpr int kAdaptMaxB = 1024;
 __device__ int unit_chunk(const int* __restrict__ kv_lens, int B, int N_kv, int chunk, int cap,
                           int HG, int nwaves) {
@@ -92,7 +92,7 @@ __device__ int unit_chunk(const int* __restrict__ kv_lens, int B, int N_kv, int 
   constexpr int PER = kAdaptMaxB / 64;
   const int lane = (int)threadIdx.x & 63;
   float len[PER];
-  float total = 0.f;
+  float total = 0.f, nb = 0.f;
   int lo = N_kv, hi = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -100,6 +100,7 @@ __device__ int unit_chunk(const int* __restrict__ kv_lens, int B, int N_kv, int 
     const int n = b < B ? min(max(kv_lens ? kv_lens[b] : N_kv, 0), N_kv) : -1;
     len[i] = (float)max(n, 0);
     total += len[i];
+    nb += n > 0 ? 1.f : 0.f;
     if (n >= 0) {
       lo = min(lo, n);
       hi = max(hi, n);
@@ -108,16 +109,23 @@ __device__ int unit_chunk(const int* __restrict__ kv_lens, int B, int N_kv, int 
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     total += __shfl_xor(total, o);
+    nb += __shfl_xor(nb, o);
     lo = min(lo, __shfl_xor(lo, o));
     hi = max(hi, __shfl_xor(hi, o));
   }
   // every lane holds the reductions; taking lane 0's keeps the decisions (and
   // the result) in scalar registers
   total = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, total)));
+  nb = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, nb)));
   lo = __builtin_amdgcn_readfirstlane(lo);
   hi = __builtin_amdgcn_readfirstlane(hi);
-  if (total == 0.f || lo != hi) return chunk;
-  const float cf = fminf(ceilf(total * (float)HG / (float)nwaves), (float)cap);
+  if (total == 0.f) return chunk;
+  // first guess: the batch's keys over the wavefronts; with unequal lengths
+  // each request's last unit is on average half full, so the units of
+  // nb / 2 requests' worth of wavefronts are set aside (usually no step of
+  // the search below is then needed)
+  const float wv = lo == hi ? (float)nwaves : fmaxf((float)nwaves - 0.5f * nb * (float)HG, 0.5f * (float)nwaves);
+  const float cf = fminf(ceilf(total * (float)HG / wv), (float)cap);
   int c = ((int)cf + kStepKeys - 1) / kStepKeys * kStepKeys;
   c = c < chunk ? chunk : (c > cap ? cap : c);
   for (int it = 0; it < 32 && c < cap; ++it) {
@@ -152,8 +160,8 @@ __device__ __forceinline__ u32x2_t fp8x4_to_bf16(uint32_t w) {
 // into LDS (V); the dequantisation scales are applied to the score scale and,
 // in the merge, to the output.
 template <class TT, int D, int NG, bool PAGED, bool FP8>
-__device__ __forceinline__ void wave_unit(const SplitParams& P, int chunk, int b, int hk, int qg,
-                                          int split, int len, uint16_t* sV) {
+__device__ __forceinline__ void wave_unit(const SplitParams& P, int chunk, int nsplit, int b, int hk,
+                                          int qg, int split, int len, uint16_t* sV) {
   constexpr int VST = DecLds<D>::VST;
   constexpr int KS = D / 32;        // k-steps of the score MFMA
   constexpr int DB = D / 16;        // 16-wide output blocks
@@ -381,7 +389,7 @@ __device__ __forceinline__ void wave_unit(const SplitParams& P, int chunk, int b
     float lj = l[j] + __shfl_xor(l[j], 16);
     lj = half_sum(lj);
     if (c16 < ncols[j]) {
-      const int64_t row = (qrow0 + col0[j] + c16) * P.splits + split;
+      const int64_t row = (qrow0 + col0[j] + c16) * nsplit + split;
       float* pu = P.part_u + row * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -412,6 +420,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(const Split
   const int nw = (int)gridDim.x * 4;
   const int B = P.B;
   const int chunk = unit_chunk(P.kv_lens, B, P.N_kv, P.chunk, P.chunk_cap, HG, nw);
+  // partials of a query row sit in consecutive slots, one per split of the
+  // chosen chunk (never more than the plan's splits: the chunk only grows)
+  const int nsplit = (P.N_kv + chunk - 1) / chunk;
   auto len_of = [&](int b) {
     const int n = P.kv_lens ? P.kv_lens[b] : P.N_kv;
     return min(max(n, 0), P.N_kv);
@@ -431,7 +442,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(const Split
       }
     }
     if (cb >= B) break;
-    wave_unit<TT, D, NG, PAGED, FP8>(P, chunk, cb, hg / ngroups, hg - (hg / ngroups) * ngroups,
+    wave_unit<TT, D, NG, PAGED, FP8>(P, chunk, nsplit, cb, hg / ngroups, hg - (hg / ngroups) * ngroups,
                                      c - cstart, lb, sV);
   }
 }
@@ -445,7 +456,7 @@ template <class TT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part_u, const float* __restrict__ part_ml,
     const int* __restrict__ kv_lens, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int rows_per_b, int N_kv, int splits, int chunk, int chunk_cap, int HG, int nwaves, int BH,
+    int rows_per_b, int N_kv, int chunk, int chunk_cap, int HG, int nwaves, int BH,
     float out_scale) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int PER = D / 64;  // columns per lane
@@ -458,7 +469,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   // the split kernel's units: the same function of the same inputs
   const int ce = unit_chunk(kv_lens, BH / rows_per_b, N_kv, chunk, chunk_cap, HG, nwaves);
   const int ns = (len + ce - 1) / ce;
-  const int64_t row0 = (int64_t)bh * splits;
+  const int64_t row0 = (int64_t)bh * ((N_kv + ce - 1) / ce);
   float M = kNegInf;
   for (int s = lane; s < ns; s += 64) M = fmaxf(M, part_ml[(row0 + s) * 2]);
 #pragma unroll
@@ -530,7 +541,6 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   P.N_q = a.N_q;
   P.N_kv = a.N_kv;
   P.causal = a.causal;
-  P.splits = a.splits;
   P.chunk = a.chunk;
   P.chunk_cap = a.chunk_cap;
   P.scale_log2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
@@ -541,9 +551,8 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int BH = a.B * a.H_q * a.N_q;
   return launch_kernel(decode_merge_kernel<TT, D>, dim3((BH + 3) / 4), dim3(256), st, a.part_u,
-                       a.part_ml, a.kv_lens, (uint16_t*)a.o, a.lse, a.H_q * a.N_q, a.N_kv, a.splits,
-                       a.chunk, a.chunk_cap, a.H_kv * ngroups, (int)grid.x * 4, BH,
-                       FP8 ? a.v_scale : 1.f);
+                       a.part_ml, a.kv_lens, (uint16_t*)a.o, a.lse, a.H_q * a.N_q, a.N_kv, a.chunk,
+                       a.chunk_cap, a.H_kv * ngroups, (int)grid.x * 4, BH, FP8 ? a.v_scale : 1.f);
 }
 
 template <class TT, bool FP8>
@@ -566,11 +575,14 @@ hipError_t launch_dtype(const DecodeArgs& a, hipStream_t st) {
 
 DecodePlan decode_plan(int B, int H_q, int H_kv, int N_q, int N_kv, int d, bool paged,
                        size_t max_workspace) {
-  // The persistent kernel hands chunks out round-robin to wavefronts. Chunks of
-  // up to 2048 keys (1 MB of K and V at d = 128) keep ragged lengths balanced
-  // while each wavefront's start-up latency (query and first K/V loads) stays
-  // a few percent of its chunk; short caches use chunks of at least 128 keys.
-  int64_t chunk = ((int64_t)N_kv + 15) / 16;
+  // The persistent kernel hands chunks out round-robin to wavefronts. The
+  // plan's chunk is the finest split the kernels may use (they raise it from
+  // the actual lengths, unit_chunk): about N_kv / 64 keys for one new token
+  // per request, so that short requests in a long cache still spread over the
+  // grid, and N_kv / 16 for more tokens, whose partials are N_q times larger;
+  // at least 128 keys and at most 2048 (1 MB of K and V at d = 128).
+  const int64_t target = N_q <= 1 ? 64 : 16;
+  int64_t chunk = ((int64_t)N_kv + target - 1) / target;
   chunk = ((chunk + kWaveKeys * 4 - 1) / (kWaveKeys * 4)) * (kWaveKeys * 4);
   if (chunk < 128) chunk = 128;
   if (chunk > 2048) chunk = 2048;

@@ -205,10 +205,21 @@ def test_tuning_defaults_come_from_the_environment_once():
 
 
 def test_decode_workspace_follows_the_chunk_knob():
-    base = L.attn_decode_workspace_size(2, 8, 2, 1, 4096, 128, E.ATTN_BF16)
+    base = L.attn_decode_workspace_size(2, 8, 2, 1, 16384, 128, E.ATTN_BF16)
     with E.tuning(decode_chunk=128):
-        fine = L.attn_decode_workspace_size(2, 8, 2, 1, 4096, 128, E.ATTN_BF16)
-    assert fine == 2 * 8 * 1 * (4096 // 128) * 130 * 4 and fine > base
+        fine = L.attn_decode_workspace_size(2, 8, 2, 1, 16384, 128, E.ATTN_BF16)
+    assert fine == 2 * 8 * 1 * (16384 // 128) * 130 * 4 and fine > base
+
+
+def test_decode_plan_splits_finer_for_one_token():
+    """The plan's finest split: about N_kv / 64 keys for one new token per
+    request, N_kv / 16 for more (partials N_q times larger), within
+    [128, 2048] keys."""
+    per = lambda nq: 2 * 8 * nq * 130 * 4
+    assert L.attn_decode_workspace_size(2, 8, 2, 1, 32768, 128, E.ATTN_BF16) == per(1) * 64
+    assert L.attn_decode_workspace_size(2, 8, 2, 4, 32768, 128, E.ATTN_BF16) == per(4) * 16
+    assert L.attn_decode_workspace_size(2, 8, 2, 1, 4096, 128, E.ATTN_BF16) == per(1) * 32
+    assert L.attn_decode_workspace_size(2, 8, 2, 1, 262144, 128, E.ATTN_BF16) == per(1) * 128
 
 
 def dfn(Nq=1, dtype=E.ATTN_BF16, lens=None, **kw):
