@@ -203,12 +203,17 @@ def test_decode_rows_mode_both_kernel_forms(case, form, tune):
                  seed=zlib.crc32(repr((case, form)).encode()) % 10000, Nq=Nq, causal=True)
 
 
-@pytest.mark.parametrize("ragged", [False, True], ids=["uniform", "ragged"])
-def test_decode_device_chosen_split_matches_oracle(ragged):
+@pytest.mark.parametrize("mix", ["uniform", "ragged", "short"])
+def test_decode_device_chosen_split_matches_oracle(mix):
     """Enough (request, KV head) pairs that the grid is full: the kernels then
     raise the split size on the device from the actual lengths (to about one
-    unit per wavefront), and the merge must find the same splits."""
-    lens = np.random.default_rng(7).integers(1, 8193, size=40) if ragged else None
+    unit per wavefront), and the merge must find the same splits. "short":
+    requests of at most 600 keys in an 8192-position cache, where the split
+    stays at the plan's finest (128 keys) and each request spreads over
+    several wavefronts."""
+    rng = np.random.default_rng(7)
+    lens = {"uniform": None, "ragged": rng.integers(1, 8193, size=40),
+            "short": rng.integers(1, 601, size=40)}[mix]
     _decode_case(40, 32, 4, 8192, 64, "bf16", lens, seed=96)
     _decode_case(40, 32, 4, 8192, 64, "bf16", lens, seed=97, Nq=3, causal=True)
 
